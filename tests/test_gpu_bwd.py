@@ -1,0 +1,92 @@
+"""GPU parity of the backward ring steps against the CPU oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from zz_testlib import TOL, Case, max_abs, rel_l2, to_np
+
+pytestmark = pytest.mark.gpu
+
+zz = pytest.importorskip("zigzag_ring_attention_amd")
+
+
+def gpu_backward(case):
+    o_acc, lse = zz.ring_attention_fwd(case.plan, case.qz, case.kz, case.vz)
+    o_zz = zz.finalize_fwd(case.plan, o_acc, unpermute=False)
+    dq, dk, dv = zz.ring_attention_bwd(case.plan, case.qz, case.kz, case.vz, o_zz, case.doz, lse)
+    # back to packed order (fp32)
+    return [to_np(x)[case.dst] for x in (dq, dk, dv)]
+
+
+def check_grads(case, tol):
+    got = gpu_backward(case)
+    want = oracle.attn_bwd(case.q, case.k, case.v, case.do, case.cu, case.scale)
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        # bf16 rounding of dS and P is relative: where gradients grow past 1
+        # (sharp softmax) the max-abs gate scales with their peak magnitude.
+        gate = tol["abs"] * max(1.0, float(np.abs(w).max()))
+        assert max_abs(g, w) < gate, (name, max_abs(g, w), gate)
+        assert rel_l2(g, w) < tol["rel"], (name, rel_l2(g, w))
+
+
+@pytest.mark.parametrize("lengths,cp,hq,hkv,d", [
+    ((96, 64, 96), 2, 2, 2, 32),
+    ((8, 24, 16), 4, 4, 2, 64),
+    ((40, 24), 1, 2, 1, 32),
+    ((200, 56), 2, 4, 2, 32),
+])
+def test_backward_fp32(lengths, cp, hq, hkv, d):
+    case = Case(lengths, cp, hq, hkv, d, "f32", 21, with_do=True)
+    check_grads(case, TOL["f32"])
+
+
+@pytest.mark.parametrize("lengths,cp,hq,hkv,d,q_scale", [
+    ((128, 256, 64), 2, 4, 2, 128, 1.0),
+    ((16, 48, 528, 8), 4, 8, 1, 128, 1.0),
+    ((512,), 4, 8, 1, 128, 4.0),
+])
+def test_backward_bf16(lengths, cp, hq, hkv, d, q_scale):
+    case = Case(lengths, cp, hq, hkv, d, "bf16", 23, with_do=True, q_scale=q_scale)
+    check_grads(case, TOL["bf16"])
+
+
+def test_backward_per_rank_equals_all_ranks():
+    import torch
+    case = Case((128, 256, 64), 2, 4, 2, 128, "bf16", 3, with_do=True)
+    o_acc, lse = zz.ring_attention_fwd(case.plan, case.qz, case.kz, case.vz)
+    o_zz = zz.finalize_fwd(case.plan, o_acc)
+    delta = zz.bwd_preprocess(case.plan, o_zz, case.doz)
+    outs = []
+    for per_rank in (False, True):
+        dq = torch.zeros((case.T, case.hq, case.d), device="cuda")
+        dk = torch.zeros((case.T, case.hkv, case.d), device="cuda")
+        dv = torch.zeros_like(dk)
+        for s in range(case.cp):
+            ranks = range(case.cp) if per_rank else [zz.ALL_RANKS]
+            for r in ranks:
+                zz.varlen_ring_step_bwd(case.plan, r, s, case.qz, case.kz, case.vz, case.doz, lse, delta, dq, dk, dv)
+        outs.append((dq, dk, dv))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_bwd_preprocess_is_rowsum():
+    import torch
+    case = Case((64, 192), 2, 4, 2, 128, "bf16", 8, with_do=True)
+    o = synthetic.randn_qkv(99, case.T, case.hq, case.hkv, case.d, "bf16")[0].cuda()
+    delta = zz.bwd_preprocess(case.plan, o, case.doz)
+    want = (o.double() * case.doz.double()).sum(-1).T.contiguous()
+    assert max_abs(to_np(delta), want.cpu().numpy()) < 1e-4
+
+
+def test_finalize_bwd_casts_and_unpermutes():
+    import torch
+    case = Case((64, 192), 2, 4, 2, 128, "bf16", 8)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    dq = torch.randn((case.T, case.hq, case.d), device="cuda", generator=g)
+    dk = torch.randn((case.T, case.hkv, case.d), device="cuda", generator=g)
+    dv = torch.randn((case.T, case.hkv, case.d), device="cuda", generator=g)
+    a, b, c = zz.finalize_bwd(case.plan, dq, dk, dv, unpermute=True)
+    for x, y in ((a, dq), (b, dk), (c, dv)):
+        assert torch.equal(x, zz.zigzag_unpermute(case.plan, y.to(torch.bfloat16)))

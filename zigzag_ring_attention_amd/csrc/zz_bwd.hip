@@ -1,0 +1,249 @@
+// Backward ring step of zigzag varlen attention (FlagScale PR #910: the
+// per-step backward of a ring driver).  With the global LSE of the merged
+// forward, a step's contribution is a plain sum:
+//   P = exp(S - LSE), dP = dO V^T, dS = P (dP - delta), delta = rowsum(dO O)
+//   dQ_r += scale dS K_j,  dK_j += scale dS^T Q_r,  dV_j += P^T dO_r
+// summed over the query heads of each key/value group.
+//
+// Two kernels per step, neither uses atomics:
+//  * dkv (key-major): a workgroup owns up to 128 keys of shard j (4 waves x 32
+//    keys) and one key/value head.  It walks every query head of the group and
+//    every listed query tile (up to 64 rows, staged in LDS with its LSE and
+//    delta), forming S and dP with the keys in the lane dimension, so that P
+//    and dS are directly the operands of dV^T += dO^T P and dK^T += Q^T dS.
+//  * dq (query-major): like the forward step, S^T and dP^T with the queries in
+//    the lane dimension, then dQ^T += K^T dS^T.
+// Fully masked tiles are never visited (tile lists from the planner).
+
+#include "zz_mfma.h"
+
+namespace zz {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdArgs {
+    const void *q, *k, *v, *dout;
+    const float *lse, *delta;
+    float *dq, *dk, *dv;
+    const WorkItem *items;
+    const int32_t *order;
+    const TileRec *tiles;
+    int64_t T;
+    int32_t n, hq, hkv;
+    float scale, scale_log2;
+};
+
+// Read-add-write of a lane's column of a transposed accumulator (C layout:
+// register i of block b is element 32*b + c_row(i, l/32) of the row).
+template <int NB>
+__device__ __forceinline__ void add_row(float *row, const f32x16 (&acc)[NB], float mul, int hh) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            float4 *dst = reinterpret_cast<float4 *>(row + 32 * b + c_row(4 * i4, hh));
+            float4 o = *dst;
+            o.x += acc[b][4 * i4 + 0] * mul;
+            o.y += acc[b][4 * i4 + 1] * mul;
+            o.z += acc[b][4 * i4 + 2] * mul;
+            o.w += acc[b][4 * i4 + 3] * mul;
+            *dst = o;
+        }
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+constexpr int kQT = 64;   // query rows per streamed tile
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+bwd_dkv_kernel(BwdArgs a) {
+    using M = Mfma<T, D>;
+    constexpr int LD = M::LD;
+    constexpr int NB = D / 32;
+    __shared__ __attribute__((aligned(16))) T Qs[kQT * LD];
+    __shared__ __attribute__((aligned(16))) T Ds[kQT * LD];
+    __shared__ float lse_s[kQT], dlt_s[kQT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+    const int kvh = blockIdx.y;
+    const int G = a.hq / a.hkv;
+    const WorkItem it = a.items[a.order ? a.order[blockIdx.x] : blockIdx.x];
+    const int nkey = it.a1 - it.a0;
+    const int kk = wave * 32 + (lane & 31);          // key offset in the item
+    const bool key_ok = kk < nkey;
+    const bool wave_on = wave * 32 < nkey;
+    const int64_t krow = (int64_t)it.shard * a.n + it.a0 + kk;   // zigzag row of this lane's key
+    const int64_t qrow0 = (int64_t)it.rank * a.n;
+    const T *q = static_cast<const T *>(a.q);
+    const T *dout = static_cast<const T *>(a.dout);
+
+    typename M::Op kop[M::KS], vop[M::KS];
+    if (key_ok) {
+        M::load_row_op(kop, static_cast<const T *>(a.k) + (krow * a.hkv + kvh) * D, hh);
+        M::load_row_op(vop, static_cast<const T *>(a.v) + (krow * a.hkv + kvh) * D, hh);
+    } else {
+        M::zero_op(kop);
+        M::zero_op(vop);
+    }
+    f32x16 dk[NB], dv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dk[b][i] = dv[b][i] = 0.0f;
+
+    for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
+        for (int t = it.tbeg; t < it.tend; ++t) {
+            const TileRec tr = a.tiles[t];
+            const int nq = tr.b1 - tr.b0;
+            __syncthreads();
+            load_tile<T, D, kThreads>(Qs, q, qrow0 + tr.b0, nq, kQT, a.hq, h, tid);
+            load_tile<T, D, kThreads>(Ds, dout, qrow0 + tr.b0, nq, kQT, a.hq, h, tid);
+            if (tid < kQT) {
+                const bool ok = tid < nq;
+                lse_s[tid] = ok ? a.lse[(int64_t)h * a.T + qrow0 + tr.b0 + tid] * kLog2e : 0.0f;
+                dlt_s[tid] = ok ? a.delta[(int64_t)h * a.T + qrow0 + tr.b0 + tid] : 0.0f;
+            }
+            __syncthreads();
+            if (!wave_on) continue;
+#pragma unroll
+            for (int qb = 0; qb < kQT / 32; ++qb) {
+                if (qb * 32 >= nq) break;
+                f32x16 s, dp;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+                M::gemm_rows_lds(s, Qs + (qb * 32 + (lane & 31)) * LD, kop, hh);
+                M::gemm_rows_lds(dp, Ds + (qb * 32 + (lane & 31)) * LD, vop, hh);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int qq = qb * 32 + c_row(i, hh);
+                    const bool vis = qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk);
+                    const float p = vis ? __builtin_amdgcn_exp2f(s[i] * a.scale_log2 - lse_s[qq]) : 0.0f;
+                    s[i] = p;
+                    dp[i] = p * (dp[i] - dlt_s[qq]);
+                }
+                M::gemm_tr_c(dv, Ds, qb * 32, s, lane);
+                M::gemm_tr_c(dk, Qs, qb * 32, dp, lane);
+            }
+        }
+    }
+    if (!key_ok) return;
+    add_row<NB>(a.dk + (krow * a.hkv + kvh) * D, dk, a.scale, hh);
+    add_row<NB>(a.dv + (krow * a.hkv + kvh) * D, dv, 1.0f, hh);
+}
+
+// ---------------------------------------------------------------- dQ
+
+constexpr int kKT = 64;   // keys per streamed tile
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+bwd_dq_kernel(BwdArgs a) {
+    using M = Mfma<T, D>;
+    constexpr int LD = M::LD;
+    constexpr int NB = D / 32;
+    __shared__ __attribute__((aligned(16))) T Ks[kKT * LD];
+    __shared__ __attribute__((aligned(16))) T Vs[kKT * LD];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+    const int head = blockIdx.y;
+    const int kvh = head / (a.hq / a.hkv);
+    const WorkItem it = a.items[a.order ? a.order[blockIdx.x] : blockIdx.x];
+    const int nq = it.a1 - it.a0;
+    const int qq = wave * 32 + (lane & 31);
+    const bool row_ok = qq < nq;
+    const bool wave_on = wave * 32 < nq;
+    const int64_t zrow = (int64_t)it.rank * a.n + it.a0 + qq;
+    const T *k = static_cast<const T *>(a.k);
+    const T *v = static_cast<const T *>(a.v);
+
+    typename M::Op qop[M::KS], dop[M::KS];
+    float lse2 = 0.0f, dlt = 0.0f;
+    if (row_ok) {
+        M::load_row_op(qop, static_cast<const T *>(a.q) + (zrow * a.hq + head) * D, hh);
+        M::load_row_op(dop, static_cast<const T *>(a.dout) + (zrow * a.hq + head) * D, hh);
+        lse2 = a.lse[(int64_t)head * a.T + zrow] * kLog2e;
+        dlt = a.delta[(int64_t)head * a.T + zrow];
+    } else {
+        M::zero_op(qop);
+        M::zero_op(dop);
+    }
+    f32x16 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
+    const int64_t kv_row0 = (int64_t)it.shard * a.n;
+
+    for (int t = it.tbeg; t < it.tend; ++t) {
+        const TileRec tr = a.tiles[t];
+        const int nk = tr.b1 - tr.b0;
+        __syncthreads();
+        load_tile<T, D, kThreads>(Ks, k, kv_row0 + tr.b0, nk, kKT, a.hkv, kvh, tid);
+        load_tile<T, D, kThreads>(Vs, v, kv_row0 + tr.b0, nk, kKT, a.hkv, kvh, tid);
+        __syncthreads();
+        if (!wave_on) continue;
+#pragma unroll
+        for (int kb = 0; kb < kKT / 32; ++kb) {
+            if (kb * 32 >= nk) break;
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+            M::gemm_rows_lds(s, Ks + (kb * 32 + (lane & 31)) * LD, qop, hh);
+            M::gemm_rows_lds(dp, Vs + (kb * 32 + (lane & 31)) * LD, dop, hh);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int kk = kb * 32 + c_row(i, hh);
+                const bool vis = kk < nk && row_ok && tile_visible(tr.kind, tr.delta, qq, kk);
+                const float p = vis ? __builtin_amdgcn_exp2f(s[i] * a.scale_log2 - lse2) : 0.0f;
+                dp[i] = p * (dp[i] - dlt);
+            }
+            M::gemm_tr_c(acc, Ks, kb * 32, dp, lane);
+        }
+    }
+    if (!row_ok) return;
+    add_row<NB>(a.dq + (zrow * a.hq + head) * D, acc, a.scale, hh);
+}
+
+template <typename T, int D>
+hipError_t launch_t(const zz_plan *p, int rank, int step, BwdArgs a, hipStream_t st) {
+    const Launch Lkv = launch_items(p, ZZ_PASS_BWD_DKV, rank, step);
+    if (Lkv.n > 0) {
+        a.items = Lkv.items; a.order = Lkv.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DKV);
+        hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), dim3(Lkv.n, p->hkv), dim3(kThreads), 0, st, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const Launch Lq = launch_items(p, ZZ_PASS_BWD_DQ, rank, step);
+    if (Lq.n > 0) {
+        a.items = Lq.items; a.order = Lq.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DQ);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(Lq.n, p->hq), dim3(kThreads), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k, const void *v,
+                           const void *dout, const float *lse, const float *delta, float *dq, float *dk,
+                           float *dv, hipStream_t st) {
+    BwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = delta;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.items = nullptr; a.order = nullptr; a.tiles = nullptr;
+    a.T = p->T; a.n = (int32_t)(p->T / p->cp); a.hq = p->hq; a.hkv = p->hkv;
+    a.scale = (float)(1.0 / std::sqrt((double)p->d));
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
+    if (p->dtype == ZZ_BF16) {
+        if (p->d == 32) return launch_t<bf16, 32>(p, rank, step, a, st);
+        if (p->d == 64) return launch_t<bf16, 64>(p, rank, step, a, st);
+        return launch_t<bf16, 128>(p, rank, step, a, st);
+    }
+    if (p->d == 32) return launch_t<float, 32>(p, rank, step, a, st);
+    if (p->d == 64) return launch_t<float, 64>(p, rank, step, a, st);
+    return launch_t<float, 128>(p, rank, step, a, st);
+}
+
+}  // namespace zz

@@ -1,0 +1,271 @@
+// C ABI of libzz (declared in include/zz.h): argument checks, then launches.
+// Nothing here throws across the ABI; every failure becomes a zz_status with a
+// per-thread message.
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+
+#include "zz_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+zz_status fail(zz_status s, const std::string &msg) {
+    g_err = msg;
+    return s;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+zz_status check_plan(const zz_plan *p, bool need_upload = true) {
+    if (!p) return fail(ZZ_ERR_ARG, "null plan");
+    if (need_upload && !p->d_ws) return fail(ZZ_ERR_STATE, "plan not uploaded (call zz_plan_upload)");
+    return ZZ_OK;
+}
+
+zz_status check_rank_step(const zz_plan *p, int32_t rank, int32_t step, bool allow_all_rank) {
+    if (step < 0 || step >= p->cp) return fail(ZZ_ERR_ARG, "step out of range");
+    if (rank == ZZ_ALL_RANKS && allow_all_rank) return ZZ_OK;
+    if (rank < 0 || rank >= p->cp) return fail(ZZ_ERR_ARG, "rank out of range");
+    return ZZ_OK;
+}
+
+zz_status check_ptrs(std::initializer_list<const void *> ps) {
+    for (const void *x : ps) {
+        if (!x) return fail(ZZ_ERR_ARG, "null device pointer");
+        if (!aligned16(x)) return fail(ZZ_ERR_ALIGN, "device pointer not 16-byte aligned");
+    }
+    return ZZ_OK;
+}
+
+zz_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ZZ_OK;
+    return fail(ZZ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define ZZ_TRY(x)                      \
+    do {                               \
+        zz_status _s = (x);            \
+        if (_s != ZZ_OK) return _s;    \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *zz_status_str(zz_status s) {
+    switch (s) {
+        case ZZ_OK: return "ok";
+        case ZZ_ERR_ARG: return "invalid argument";
+        case ZZ_ERR_SHAPE: return "inconsistent shape";
+        case ZZ_ERR_DTYPE: return "unsupported dtype";
+        case ZZ_ERR_ALIGN: return "misaligned pointer or row size";
+        case ZZ_ERR_WORKSPACE: return "workspace or output buffer too small";
+        case ZZ_ERR_HIP: return "HIP error";
+        case ZZ_ERR_STATE: return "plan not uploaded";
+    }
+    return "unknown status";
+}
+
+const char *zz_last_error(void) { return g_err.c_str(); }
+
+zz_status zz_plan_create(const int32_t *cu_seqlens, int32_t nseq, int32_t cp, int32_t hq,
+                         int32_t hkv, int32_t head_dim, zz_dtype dtype, int32_t bm, int32_t bn,
+                         zz_plan **out) {
+    g_err.clear();
+    std::string err;
+    zz_status s = zz::build_plan(cu_seqlens, nseq, cp, hq, hkv, head_dim, dtype, bm, bn, out, &err);
+    if (s != ZZ_OK) return fail(s, err);
+    return ZZ_OK;
+}
+
+void zz_plan_destroy(zz_plan *plan) { delete plan; }
+
+size_t zz_plan_workspace_bytes(const zz_plan *plan) { return plan ? plan->ws_bytes : 0; }
+
+zz_status zz_plan_upload(zz_plan *plan, void *d_ws, size_t ws_bytes, void *stream) {
+    ZZ_TRY(check_plan(plan, false));
+    ZZ_TRY(check_ptrs({d_ws}));
+    if (ws_bytes < plan->ws_bytes) return fail(ZZ_ERR_WORKSPACE, "workspace smaller than zz_plan_workspace_bytes");
+    hipStream_t st = (hipStream_t)stream;
+    ZZ_TRY(hip_status(hipMemcpyAsync(d_ws, plan->image.data(), plan->ws_bytes, hipMemcpyHostToDevice, st),
+                      "plan upload"));
+    // The host image must outlive the copy: wait for it here, once per plan.
+    ZZ_TRY(hip_status(hipStreamSynchronize(st), "plan upload sync"));
+    plan->d_ws = (const uint8_t *)d_ws;
+    return ZZ_OK;
+}
+
+zz_status zz_plan_shape(const zz_plan *p, int64_t *total_tokens, int32_t *nseq, int32_t *cp,
+                        int32_t *hq, int32_t *hkv, int32_t *head_dim, int32_t *dtype) {
+    ZZ_TRY(check_plan(p, false));
+    if (total_tokens) *total_tokens = p->T;
+    if (nseq) *nseq = p->nseq;
+    if (cp) *cp = p->cp;
+    if (hq) *hq = p->hq;
+    if (hkv) *hkv = p->hkv;
+    if (head_dim) *head_dim = p->d;
+    if (dtype) *dtype = (int32_t)p->dtype;
+    return ZZ_OK;
+}
+
+zz_status zz_plan_local_cu_seqlens(const zz_plan *p, int32_t *out) {
+    ZZ_TRY(check_plan(p, false));
+    if (!out) return fail(ZZ_ERR_ARG, "null output");
+    for (int32_t i = 0; i <= p->nseq; ++i) out[i] = p->cu[i] / p->cp;
+    return ZZ_OK;
+}
+
+zz_status zz_plan_zigzag_dst(const zz_plan *p, int64_t *out) {
+    ZZ_TRY(check_plan(p, false));
+    if (!out) return fail(ZZ_ERR_ARG, "null output");
+    for (int64_t z = 0; z < p->T; ++z) out[p->src[(size_t)z]] = z;
+    return ZZ_OK;
+}
+
+zz_status zz_plan_tile_shape(const zz_plan *p, zz_pass pass, int32_t *bm, int32_t *bn) {
+    ZZ_TRY(check_plan(p, false));
+    if (pass < ZZ_PASS_FWD || pass > ZZ_PASS_BWD_DKV) return fail(ZZ_ERR_ARG, "bad pass");
+    if (bm) *bm = p->pass[pass].bm;
+    if (bn) *bn = p->pass[pass].bn;
+    return ZZ_OK;
+}
+
+zz_status zz_plan_tiles(const zz_plan *p, zz_pass pass, int32_t rank, int32_t step, int32_t *out,
+                        int64_t cap, int64_t *n) {
+    ZZ_TRY(check_plan(p, false));
+    if (pass < ZZ_PASS_FWD || pass > ZZ_PASS_BWD_DKV) return fail(ZZ_ERR_ARG, "bad pass");
+    ZZ_TRY(check_rank_step(p, rank, step, false));
+    if (!n || (cap > 0 && !out)) return fail(ZZ_ERR_ARG, "null output");
+    const zz::PassTables &t = p->pass[pass];
+    struct Q { int32_t q0, q1, k0, k1, kind; };
+    std::vector<Q> v;
+    const int64_t b = t.rank_off[(size_t)step * p->cp + rank], e = t.rank_off[(size_t)step * p->cp + rank + 1];
+    for (int64_t u = b; u < e; ++u) {
+        const zz::WorkItem &it = t.items[(size_t)u];
+        for (int32_t x = it.tbeg; x < it.tend; ++x) {
+            const zz::TileRec &tr = t.tiles[(size_t)x];
+            if (t.key_major) v.push_back(Q{tr.b0, tr.b1, it.a0, it.a1, tr.kind});
+            else v.push_back(Q{it.a0, it.a1, tr.b0, tr.b1, tr.kind});
+        }
+    }
+    std::sort(v.begin(), v.end(), [](const Q &a, const Q &c) {
+        return a.q0 != c.q0 ? a.q0 < c.q0 : a.k0 < c.k0;
+    });
+    *n = (int64_t)v.size();
+    for (int64_t u = 0; u < std::min<int64_t>(cap, (int64_t)v.size()); ++u) {
+        const Q &x = v[(size_t)u];
+        int32_t *o = out + 5 * u;
+        o[0] = x.q0; o[1] = x.q1; o[2] = x.k0; o[3] = x.k1; o[4] = x.kind;
+    }
+    if ((int64_t)v.size() > cap) return fail(ZZ_ERR_WORKSPACE, "tile output capacity too small");
+    return ZZ_OK;
+}
+
+zz_status zz_plan_pair_counts(const zz_plan *p, zz_pass pass, int32_t rank, int32_t step,
+                              int64_t *useful, int64_t *issued) {
+    ZZ_TRY(check_plan(p, false));
+    if (pass < ZZ_PASS_FWD || pass > ZZ_PASS_BWD_DKV) return fail(ZZ_ERR_ARG, "bad pass");
+    if (rank != ZZ_ALL_RANKS && (rank < 0 || rank >= p->cp)) return fail(ZZ_ERR_ARG, "rank out of range");
+    if (step != ZZ_ALL_STEPS && (step < 0 || step >= p->cp)) return fail(ZZ_ERR_ARG, "step out of range");
+    const zz::PassTables &t = p->pass[pass];
+    int64_t u = 0, is = 0;
+    for (int32_t s = 0; s < p->cp; ++s)
+        for (int32_t r = 0; r < p->cp; ++r) {
+            if ((step != ZZ_ALL_STEPS && s != step) || (rank != ZZ_ALL_RANKS && r != rank)) continue;
+            u += t.useful[(size_t)s * p->cp + r];
+            is += t.issued[(size_t)s * p->cp + r];
+        }
+    if (useful) *useful = u;
+    if (issued) *issued = is;
+    return ZZ_OK;
+}
+
+zz_status zz_zigzag_permute(const zz_plan *p, const void *x_packed, void *x_zz, int64_t row_bytes,
+                            void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_ptrs({x_packed, x_zz}));
+    if (row_bytes <= 0 || row_bytes % 16) return fail(ZZ_ERR_ALIGN, "row_bytes must be a positive multiple of 16");
+    if (x_packed == x_zz) return fail(ZZ_ERR_ARG, "in-place permute is not supported");
+    return hip_status(zz::launch_permute(p, x_packed, x_zz, row_bytes, false, (hipStream_t)stream), "permute");
+}
+
+zz_status zz_zigzag_unpermute(const zz_plan *p, const void *x_zz, void *x_packed, int64_t row_bytes,
+                              void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_ptrs({x_packed, x_zz}));
+    if (row_bytes <= 0 || row_bytes % 16) return fail(ZZ_ERR_ALIGN, "row_bytes must be a positive multiple of 16");
+    if (x_packed == x_zz) return fail(ZZ_ERR_ARG, "in-place unpermute is not supported");
+    return hip_status(zz::launch_permute(p, x_zz, x_packed, row_bytes, true, (hipStream_t)stream), "unpermute");
+}
+
+zz_status zz_varlen_ring_step_fwd(const zz_plan *p, int32_t rank, int32_t step, const void *q_zz,
+                                  const void *k_zz, const void *v_zz, float *o_acc, float *lse_acc,
+                                  int32_t merge, void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_rank_step(p, rank, step, true));
+    ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, o_acc, lse_acc}));
+    if (merge != 0 && merge != 1) return fail(ZZ_ERR_ARG, "merge must be 0 or 1");
+    return hip_status(zz::launch_fwd_step(p, rank, step, q_zz, k_zz, v_zz, o_acc, lse_acc, merge,
+                                          (hipStream_t)stream), "varlen_ring_step_fwd");
+}
+
+zz_status zz_lse_merge(float *o_acc, float *lse_acc, const float *o_part, const float *lse_part,
+                       int64_t rows, int32_t heads, int32_t head_dim, void *stream) {
+    ZZ_TRY(check_ptrs({o_acc, lse_acc, o_part, lse_part}));
+    if (rows < 0 || heads < 1 || head_dim < 1 || head_dim % 4) return fail(ZZ_ERR_ARG, "bad merge shape (head_dim % 4 == 0)");
+    if (rows == 0) return ZZ_OK;
+    return hip_status(zz::launch_lse_merge(o_acc, lse_acc, o_part, lse_part, rows, heads, head_dim,
+                                           (hipStream_t)stream), "lse_merge");
+}
+
+zz_status zz_finalize_fwd(const zz_plan *p, const float *o_acc, void *o_out, int32_t unpermute,
+                          void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_ptrs({o_acc, o_out}));
+    if ((const void *)o_acc == o_out) return fail(ZZ_ERR_ARG, "o_out must not alias o_acc");
+    return hip_status(zz::launch_cast_rows(p, o_acc, o_out, p->hq, unpermute != 0, (hipStream_t)stream),
+                      "finalize_fwd");
+}
+
+zz_status zz_bwd_preprocess(const zz_plan *p, const void *o_zz, const void *do_zz, float *delta,
+                            void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_ptrs({o_zz, do_zz, delta}));
+    return hip_status(zz::launch_bwd_pre(p, o_zz, do_zz, delta, (hipStream_t)stream), "bwd_preprocess");
+}
+
+zz_status zz_varlen_ring_step_bwd(const zz_plan *p, int32_t rank, int32_t step, const void *q_zz,
+                                  const void *k_zz, const void *v_zz, const void *do_zz,
+                                  const float *lse, const float *delta, float *dq_acc,
+                                  float *dk_acc, float *dv_acc, void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_rank_step(p, rank, step, true));
+    ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc, dk_acc, dv_acc}));
+    return hip_status(zz::launch_bwd_step(p, rank, step, q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc,
+                                          dk_acc, dv_acc, (hipStream_t)stream), "varlen_ring_step_bwd");
+}
+
+zz_status zz_finalize_bwd(const zz_plan *p, const float *dq_acc, const float *dk_acc,
+                          const float *dv_acc, void *dq_out, void *dk_out, void *dv_out,
+                          int32_t unpermute, void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_ptrs({dq_acc, dk_acc, dv_acc, dq_out, dk_out, dv_out}));
+    hipStream_t st = (hipStream_t)stream;
+    ZZ_TRY(hip_status(zz::launch_cast_rows(p, dq_acc, dq_out, p->hq, unpermute != 0, st), "finalize_bwd dq"));
+    ZZ_TRY(hip_status(zz::launch_cast_rows(p, dk_acc, dk_out, p->hkv, unpermute != 0, st), "finalize_bwd dk"));
+    return hip_status(zz::launch_cast_rows(p, dv_acc, dv_out, p->hkv, unpermute != 0, st), "finalize_bwd dv");
+}
+
+zz_status zz_debug_mask(const zz_plan *p, zz_pass pass, int32_t rank, int32_t step, uint8_t *d_mask,
+                        void *stream) {
+    ZZ_TRY(check_plan(p));
+    if (pass < ZZ_PASS_FWD || pass > ZZ_PASS_BWD_DKV) return fail(ZZ_ERR_ARG, "bad pass");
+    ZZ_TRY(check_rank_step(p, rank, step, false));
+    ZZ_TRY(check_ptrs({d_mask}));
+    return hip_status(zz::launch_debug_mask(p, pass, rank, step, d_mask, (hipStream_t)stream), "debug_mask");
+}
+
+}  // extern "C"

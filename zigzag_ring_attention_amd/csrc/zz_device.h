@@ -1,0 +1,58 @@
+// Device-side helpers shared by the libzz kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "zz_internal.h"
+
+namespace zz {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Visibility inside a listed tile, shared by every kernel that applies the
+// mask and by the debug dump.  qq / kk are the query / key offsets inside the
+// tile; a PARTIAL tile comes from a diagonal chunk pair, where a key is
+// visible iff its chunk offset does not exceed the query's (causal).
+__device__ __forceinline__ bool tile_visible(int kind, int delta, int qq, int kk) {
+    return kind == ZZ_TILE_FULL || kk <= qq + delta;
+}
+
+// Log-sum-exp merge of two partial results over disjoint key sets:
+// L = log(e^a + e^b), O = e^(a-L) O_a + e^(b-L) O_b; (0, -inf) is the
+// identity.  Used both by the standalone merge and by the fused epilogue of
+// the forward step, so the two give bit-identical results.
+struct MergeWeights {
+    float wa, wb, lse;
+};
+__device__ __forceinline__ MergeWeights merge_weights(float a, float b) {
+    const float m = fmaxf(a, b);
+    if (m == -INFINITY) return MergeWeights{0.0f, 0.0f, -INFINITY};
+    const float L = m + logf(expf(a - m) + expf(b - m));
+    return MergeWeights{expf(a - L), expf(b - L), L};
+}
+__device__ __forceinline__ float merge_value(const MergeWeights &w, float oa, float ob) {
+    return fmaf(w.wa, oa, w.wb * ob);
+}
+
+// float -> bf16, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float to_float(float x) { return x; }
+    static __device__ __forceinline__ float from_float(float x) { return x; }
+};
+template <> struct Elem<bf16> {
+    static __device__ __forceinline__ float to_float(bf16 x) { return static_cast<float>(x); }
+    static __device__ __forceinline__ bf16 from_float(float x) { return to_bf16(x); }
+};
+
+}  // namespace zz

@@ -1,0 +1,215 @@
+// Forward ring step of zigzag varlen attention (FlagScale PR #910: the
+// per-step forward of a ring driver; MiniMax-01 issue #6: varlen ring
+// attention over packed data).
+//
+// One workgroup = one work item (a tile of up to 128 query rows of one rank,
+// inside one zigzag chunk) x one query head.  Four waves own 32 query rows
+// each.  The workgroup walks the item's listed key tiles of shard
+// j = (rank - step) mod CP -- fully masked tiles were pruned by the planner --
+// staging K and V tiles of up to 64 keys in LDS.  Per tile and wave:
+//   S^T = K Q^T * scale * log2(e)          (MFMA, fp32 accumulate)
+//   mask only on PARTIAL tiles (diagonal chunk pair: key offset <= query
+//   offset); keys past the ragged tile end are masked on every tile
+//   online softmax per query: running max m (exchanged between the two lane
+//   halves that hold the query's keys), rescale, exp2
+//   O^T += V^T P^T                          (MFMA, P rounded to the input dtype)
+// Epilogue: O = O^T / l, LSE = (m + log2 l) * ln 2 (natural log), written as
+// the step's partial or merged into the accumulator by log-sum-exp.
+//
+// Scale 1/sqrt(head_dim): MaxText PR #1133, scale_factor of the CP attention call.
+
+#include "zz_mfma.h"
+
+namespace zz {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per LDS tile
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    float *o, *lse;
+    const WorkItem *items;
+    const int32_t *order;
+    const TileRec *tiles;
+    int64_t T;          // total tokens
+    int32_t n;          // rows per rank = T / cp
+    int32_t hq, hkv;
+    float scale_log2;   // softmax scale * log2(e)
+    int32_t merge;
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kThreads)
+fwd_step_kernel(FwdArgs a) {
+    using M = Mfma<T, D>;
+    constexpr int LD = M::LD;
+    constexpr int NB = D / 32;   // 32-wide head-dim blocks of O^T
+    __shared__ __attribute__((aligned(16))) T Ks[kBN * LD];
+    __shared__ __attribute__((aligned(16))) T Vs[kBN * LD];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+    const int head = blockIdx.y;
+    const int kvh = head / (a.hq / a.hkv);
+    const WorkItem it = a.items[a.order ? a.order[blockIdx.x] : blockIdx.x];
+    const int nq = it.a1 - it.a0;
+    const int qq = wave * 32 + (lane & 31);          // query offset in the item
+    const bool row_ok = qq < nq;
+    const bool wave_on = wave * 32 < nq;             // wave-uniform
+    const int64_t zrow = (int64_t)it.rank * a.n + it.a0 + qq;   // zigzag row of this lane's query
+    const T *q = static_cast<const T *>(a.q);
+    const T *k = static_cast<const T *>(a.k);
+    const T *v = static_cast<const T *>(a.v);
+
+    if (it.tbeg == it.tend) {
+        // No visible key in this step: the partial is (0, -inf); merging it is a no-op.
+        if (a.merge || !row_ok) return;
+        float4 z = {0.f, 0.f, 0.f, 0.f};
+        float *orow = a.o + (zrow * a.hq + head) * D;
+        for (int e = 4 * hh; e < D; e += 8) *reinterpret_cast<float4 *>(orow + e) = z;
+        if (hh == 0) a.lse[(int64_t)head * a.T + zrow] = -INFINITY;
+        return;
+    }
+
+    typename M::Op qop[M::KS];
+    if (row_ok) M::load_row_op(qop, q + (zrow * a.hq + head) * D, hh);
+    else M::zero_op(qop);
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
+    // lsum: sum of the weights as rounded for the P.V product (normalizes O);
+    // lexp: sum of the unrounded weights (gives the LSE).
+    float m = -INFINITY, lsum = 0.0f, lexp = 0.0f;
+    const int64_t kv_row0 = (int64_t)it.shard * a.n;
+
+    for (int t = it.tbeg; t < it.tend; ++t) {
+        const TileRec tr = a.tiles[t];
+        const int nk = tr.b1 - tr.b0;
+        __syncthreads();
+        load_tile<T, D, kThreads>(Ks, k, kv_row0 + tr.b0, nk, kBN, a.hkv, kvh, tid);
+        load_tile<T, D, kThreads>(Vs, v, kv_row0 + tr.b0, nk, kBN, a.hkv, kvh, tid);
+        __syncthreads();
+        if (!wave_on) continue;
+
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+            if (kb == 0 || nk > 32) M::gemm_rows_lds(s[kb], Ks + (kb * 32 + (lane & 31)) * LD, qop, hh);
+        }
+        // scale, mask, block max
+        const bool need_mask = tr.kind != ZZ_TILE_FULL || nk < kBN;
+        float mt = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x = s[kb][i] * a.scale_log2;
+                if (need_mask) {
+                    const int kk = kb * 32 + c_row(i, hh);
+                    if (kk >= nk || !tile_visible(tr.kind, tr.delta, qq, kk)) x = -INFINITY;
+                }
+                s[kb][i] = x;
+                mt = fmaxf(mt, x);
+            }
+        mt = fmaxf(mt, swap_halves(mt, lane));
+        const float mnew = fmaxf(m, mt);
+        const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+        float ps = 0.0f, pe = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e = __builtin_amdgcn_exp2f(s[kb][i] - msafe);
+                const float p = M::round_p(e);
+                s[kb][i] = p;
+                ps += p;
+                pe += e;
+            }
+        lsum = lsum * alpha + ps;
+        lexp = lexp * alpha + pe;
+        m = mnew;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+        M::gemm_tr_c(acc, Vs, 0, s[0], lane);
+        if (nk > 32) M::gemm_tr_c(acc, Vs, 32, s[1], lane);
+    }
+    if (!row_ok) return;
+
+    // Epilogue: the lane pair (l, l^32) holds one query's keys split in two.
+    const float ltot = lsum + swap_halves(lsum, lane);
+    const float etot = lexp + swap_halves(lexp, lane);
+    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    const float lse_b = etot > 0.0f ? (m + log2f(etot)) * 0.69314718055994530942f : -INFINITY;
+    float *orow = a.o + (zrow * a.hq + head) * D;
+    float *lse_p = a.lse + (int64_t)head * a.T + zrow;
+    if (!a.merge) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                float4 w;
+                w.x = acc[b][4 * i4 + 0] * inv;
+                w.y = acc[b][4 * i4 + 1] * inv;
+                w.z = acc[b][4 * i4 + 2] * inv;
+                w.w = acc[b][4 * i4 + 3] * inv;
+                *reinterpret_cast<float4 *>(orow + 32 * b + c_row(4 * i4, hh)) = w;
+            }
+        if (hh == 0) *lse_p = lse_b;
+    } else {
+        const MergeWeights w = merge_weights(*lse_p, lse_b);
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                float4 *dst = reinterpret_cast<float4 *>(orow + 32 * b + c_row(4 * i4, hh));
+                float4 o = *dst;
+                o.x = merge_value(w, o.x, acc[b][4 * i4 + 0] * inv);
+                o.y = merge_value(w, o.y, acc[b][4 * i4 + 1] * inv);
+                o.z = merge_value(w, o.z, acc[b][4 * i4 + 2] * inv);
+                o.w = merge_value(w, o.w, acc[b][4 * i4 + 3] * inv);
+                *dst = o;
+            }
+        if (hh == 0) *lse_p = w.lse;
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_t(const zz_plan *p, const Launch &L, const void *q, const void *k, const void *v, float *o,
+                    float *lse, int merge, hipStream_t st) {
+    FwdArgs a;
+    a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+    a.items = L.items; a.order = L.order; a.tiles = dev_tiles(p, ZZ_PASS_FWD);
+    a.T = p->T; a.n = (int32_t)(p->T / p->cp); a.hq = p->hq; a.hkv = p->hkv;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
+    a.merge = merge;
+    hipLaunchKernelGGL((fwd_step_kernel<T, D>), dim3(L.n, p->hq), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k, const void *v,
+                           float *o, float *lse, int merge, hipStream_t st) {
+    const Launch L = launch_items(p, ZZ_PASS_FWD, rank, step);
+    if (L.n == 0) return hipSuccess;
+    if (p->dtype == ZZ_BF16) {
+        if (p->d == 32) return launch_t<bf16, 32>(p, L, q, k, v, o, lse, merge, st);
+        if (p->d == 64) return launch_t<bf16, 64>(p, L, q, k, v, o, lse, merge, st);
+        return launch_t<bf16, 128>(p, L, q, k, v, o, lse, merge, st);
+    }
+    if (p->d == 32) return launch_t<float, 32>(p, L, q, k, v, o, lse, merge, st);
+    if (p->d == 64) return launch_t<float, 64>(p, L, q, k, v, o, lse, merge, st);
+    return launch_t<float, 128>(p, L, q, k, v, o, lse, merge, st);
+}
+
+}  // namespace zz
