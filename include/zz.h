@@ -203,18 +203,34 @@ zz_status zz_bwd_preprocess(const zz_plan *plan, const void *o_zz, const void *d
 
 /*
  * One backward ring step (FlagScale PR #910: per-step backward).  With the
- * global LSE of the merged forward and delta from zz_bwd_preprocess, adds this
- * step's contributions: dq_acc rows of rank r, dk_acc / dv_acc rows of shard
+ * global LSE of the merged forward and delta from zz_bwd_preprocess, this
+ * step's contributions are: dq rows of rank r, and dk / dv rows of shard
  * j = (r - step) mod cp (summed over the query heads of each group).
- *  dq_acc fp32 [T, hq, d]; dk_acc, dv_acc fp32 [T, hkv, d]; zigzag layout;
- *  the caller zeroes them before the first step.  Accumulation is plain
- *  read-add-write: launches on one buffer must not overlap in time.
+ *  q_zz [T,hq,d], k_zz / v_zz [T,hkv,d], do_zz [T,hq,d]: plan dtype, zigzag.
+ *  lse, delta: fp32 [hq, T].
+ *  dq_acc fp32 [T, hq, d]; dk_acc, dv_acc fp32 [T, hkv, d]; zigzag layout.
+ *  accumulate = 1 adds the contributions (plain read-add-write: launches on
+ *  one buffer must not overlap in time); 0 overwrites the rows this step
+ *  touches (step 0 of the ring touches every row, so a driver needs no
+ *  zero-fill).
+ * zz_varlen_ring_step_bwd launches both kernels of the step; the _dkv / _dq
+ * variants launch one each (they write disjoint buffers and may run on
+ * different streams).
  * Errors: as zz_varlen_ring_step_fwd.
  */
 zz_status zz_varlen_ring_step_bwd(const zz_plan *plan, int32_t rank, int32_t step,
                                   const void *q_zz, const void *k_zz, const void *v_zz,
                                   const void *do_zz, const float *lse, const float *delta,
-                                  float *dq_acc, float *dk_acc, float *dv_acc, void *stream);
+                                  float *dq_acc, float *dk_acc, float *dv_acc, int32_t accumulate,
+                                  void *stream);
+zz_status zz_varlen_ring_step_bwd_dkv(const zz_plan *plan, int32_t rank, int32_t step,
+                                      const void *q_zz, const void *k_zz, const void *v_zz,
+                                      const void *do_zz, const float *lse, const float *delta,
+                                      float *dk_acc, float *dv_acc, int32_t accumulate, void *stream);
+zz_status zz_varlen_ring_step_bwd_dq(const zz_plan *plan, int32_t rank, int32_t step,
+                                     const void *q_zz, const void *k_zz, const void *v_zz,
+                                     const void *do_zz, const float *lse, const float *delta,
+                                     float *dq_acc, int32_t accumulate, void *stream);
 
 /*
  * Gradients to the plan dtype: dq_out [T,hq,d], dk_out/dv_out [T,hkv,d];

@@ -58,16 +58,28 @@ def test_backward_per_rank_equals_all_ranks():
     o_zz = zz.finalize_fwd(case.plan, o_acc)
     delta = zz.bwd_preprocess(case.plan, o_zz, case.doz)
     outs = []
-    for per_rank in (False, True):
+    for mode in ("all", "per_rank", "split"):
         dq = torch.zeros((case.T, case.hq, case.d), device="cuda")
         dk = torch.zeros((case.T, case.hkv, case.d), device="cuda")
         dv = torch.zeros_like(dk)
         for s in range(case.cp):
-            ranks = range(case.cp) if per_rank else [zz.ALL_RANKS]
+            ranks = range(case.cp) if mode == "per_rank" else [zz.ALL_RANKS]
             for r in ranks:
-                zz.varlen_ring_step_bwd(case.plan, r, s, case.qz, case.kz, case.vz, case.doz, lse, delta, dq, dk, dv)
+                if mode == "split":   # the two kernels of a step through their own entry points
+                    zz.varlen_ring_step_bwd_dq(case.plan, r, s, case.qz, case.kz, case.vz, case.doz, lse,
+                                               delta, dq, accumulate=True)
+                    zz.varlen_ring_step_bwd_dkv(case.plan, r, s, case.qz, case.kz, case.vz, case.doz, lse,
+                                                delta, dk, dv, accumulate=True)
+                else:
+                    zz.varlen_ring_step_bwd(case.plan, r, s, case.qz, case.kz, case.vz, case.doz, lse, delta,
+                                            dq, dk, dv, accumulate=True)
         outs.append((dq, dk, dv))
-    for a, b in zip(*outs):
+    for other in outs[1:]:
+        for a, b in zip(outs[0], other):
+            assert torch.equal(a, b)
+    # overwrite on step 0 (it touches every row) equals zero-fill + accumulate
+    dq2, dk2, dv2 = zz.ring_attention_bwd(case.plan, case.qz, case.kz, case.vz, o_zz, case.doz, lse)
+    for a, b in zip(outs[0], (dq2, dk2, dv2)):
         assert torch.equal(a, b)
 
 

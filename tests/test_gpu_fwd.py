@@ -221,4 +221,6 @@ def test_unreordered_tokens_fail_parity():
 def test_constant_value_gives_constant_output():
     case = Case((16, 48, 528, 8), 4, 8, 2, 128, "bf16", 1, const_v=0.625)
     o_acc, lse = zz.ring_attention_fwd(case.plan, case.qz, case.kz, case.vz)
-    assert max_abs(to_np(o_acc), 0.625) < 1e-5
+    # weights enter P.V rounded to bf16 while the row sum is fp32: a relative
+    # error of at most about 2^-9 on short rows
+    assert max_abs(to_np(o_acc), 0.625) < 0.625 * 2.0 ** -8

@@ -19,7 +19,8 @@ import numpy as np
 __all__ = [
     "Plan", "ZZError", "PASS_FWD", "PASS_BWD_DQ", "PASS_BWD_DKV", "ALL_RANKS", "ALL_STEPS",
     "lib", "zigzag_permute", "zigzag_unpermute", "varlen_ring_step_fwd", "lse_merge",
-    "finalize_fwd", "bwd_preprocess", "varlen_ring_step_bwd", "finalize_bwd", "debug_mask",
+    "finalize_fwd", "bwd_preprocess", "varlen_ring_step_bwd", "varlen_ring_step_bwd_dkv",
+    "varlen_ring_step_bwd_dq", "finalize_bwd", "debug_mask",
     "ring_attention_fwd", "ring_attention_bwd", "library_path",
 ]
 
@@ -70,7 +71,9 @@ def lib():
         "zz_lse_merge": ([P, P, P, P, i64, i32, i32, P], i32),
         "zz_finalize_fwd": ([P, P, P, i32, P], i32),
         "zz_bwd_preprocess": ([P, P, P, P, P], i32),
-        "zz_varlen_ring_step_bwd": ([P, i32, i32, P, P, P, P, P, P, P, P, P, P], i32),
+        "zz_varlen_ring_step_bwd": ([P, i32, i32, P, P, P, P, P, P, P, P, P, i32, P], i32),
+        "zz_varlen_ring_step_bwd_dkv": ([P, i32, i32, P, P, P, P, P, P, P, P, i32, P], i32),
+        "zz_varlen_ring_step_bwd_dq": ([P, i32, i32, P, P, P, P, P, P, P, i32, P], i32),
         "zz_finalize_bwd": ([P, P, P, P, P, P, P, i32, P], i32),
         "zz_debug_mask": ([P, i32, i32, i32, P, P], i32),
     }
@@ -276,18 +279,40 @@ def bwd_preprocess(plan: Plan, o_zz, do_zz, delta=None, stream=None):
 
 
 def varlen_ring_step_bwd(plan: Plan, rank: int, step: int, q_zz, k_zz, v_zz, do_zz, lse, delta,
-                         dq_acc, dk_acc, dv_acc, stream=None):
+                         dq_acc, dk_acc, dv_acc, accumulate: bool = True, stream=None):
     _check_qkv(plan, q_zz, k_zz, v_zz)
     _check(lib().zz_varlen_ring_step_bwd(plan.handle, rank, step, _ptr(q_zz), _ptr(k_zz), _ptr(v_zz),
                                          _ptr(do_zz), _ptr(lse), _ptr(delta), _ptr(dq_acc), _ptr(dk_acc),
-                                         _ptr(dv_acc), _stream(stream)), "zz_varlen_ring_step_bwd")
+                                         _ptr(dv_acc), 1 if accumulate else 0, _stream(stream)),
+           "zz_varlen_ring_step_bwd")
 
 
-def finalize_bwd(plan: Plan, dq_acc, dk_acc, dv_acc, unpermute: bool = False, stream=None):
+def varlen_ring_step_bwd_dkv(plan: Plan, rank: int, step: int, q_zz, k_zz, v_zz, do_zz, lse, delta,
+                             dk_acc, dv_acc, accumulate: bool = True, stream=None):
+    _check_qkv(plan, q_zz, k_zz, v_zz)
+    _check(lib().zz_varlen_ring_step_bwd_dkv(plan.handle, rank, step, _ptr(q_zz), _ptr(k_zz), _ptr(v_zz),
+                                             _ptr(do_zz), _ptr(lse), _ptr(delta), _ptr(dk_acc), _ptr(dv_acc),
+                                             1 if accumulate else 0, _stream(stream)),
+           "zz_varlen_ring_step_bwd_dkv")
+
+
+def varlen_ring_step_bwd_dq(plan: Plan, rank: int, step: int, q_zz, k_zz, v_zz, do_zz, lse, delta,
+                            dq_acc, accumulate: bool = True, stream=None):
+    _check_qkv(plan, q_zz, k_zz, v_zz)
+    _check(lib().zz_varlen_ring_step_bwd_dq(plan.handle, rank, step, _ptr(q_zz), _ptr(k_zz), _ptr(v_zz),
+                                            _ptr(do_zz), _ptr(lse), _ptr(delta), _ptr(dq_acc),
+                                            1 if accumulate else 0, _stream(stream)),
+           "zz_varlen_ring_step_bwd_dq")
+
+
+def finalize_bwd(plan: Plan, dq_acc, dk_acc, dv_acc, unpermute: bool = False, out=None, stream=None):
     import torch
-    dq = torch.empty(dq_acc.shape, dtype=plan.torch_dtype, device=dq_acc.device)
-    dk = torch.empty(dk_acc.shape, dtype=plan.torch_dtype, device=dk_acc.device)
-    dv = torch.empty(dv_acc.shape, dtype=plan.torch_dtype, device=dv_acc.device)
+    if out is not None:
+        dq, dk, dv = out
+    else:
+        dq = torch.empty(dq_acc.shape, dtype=plan.torch_dtype, device=dq_acc.device)
+        dk = torch.empty(dk_acc.shape, dtype=plan.torch_dtype, device=dk_acc.device)
+        dv = torch.empty(dv_acc.shape, dtype=plan.torch_dtype, device=dv_acc.device)
     _check(lib().zz_finalize_bwd(plan.handle, _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc), _ptr(dq), _ptr(dk),
                                  _ptr(dv), 1 if unpermute else 0, _stream(stream)), "zz_finalize_bwd")
     return dq, dk, dv
@@ -323,13 +348,16 @@ def ring_attention_fwd(plan: Plan, q_zz, k_zz, v_zz, rank: int = ALL_RANKS, o_ac
 
 
 def ring_attention_bwd(plan: Plan, q_zz, k_zz, v_zz, o_zz, do_zz, lse, stream=None):
-    """All ring steps of the backward.  Returns fp32 (dq, dk, dv) in zigzag layout."""
+    """All ring steps of the backward.  Step 0 (the diagonal shard, which
+    touches every row) overwrites, later steps accumulate.  Returns fp32
+    (dq, dk, dv) in zigzag layout."""
     import torch
     dev = q_zz.device
     delta = bwd_preprocess(plan, o_zz, do_zz, stream=stream)
-    dq = torch.zeros((plan.total, plan.hq, plan.d), dtype=torch.float32, device=dev)
-    dk = torch.zeros((plan.total, plan.hkv, plan.d), dtype=torch.float32, device=dev)
-    dv = torch.zeros((plan.total, plan.hkv, plan.d), dtype=torch.float32, device=dev)
+    dq = torch.empty((plan.total, plan.hq, plan.d), dtype=torch.float32, device=dev)
+    dk = torch.empty((plan.total, plan.hkv, plan.d), dtype=torch.float32, device=dev)
+    dv = torch.empty((plan.total, plan.hkv, plan.d), dtype=torch.float32, device=dev)
     for s in range(plan.cp):
-        varlen_ring_step_bwd(plan, ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv, stream)
+        varlen_ring_step_bwd(plan, ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv,
+                             accumulate=s > 0, stream=stream)
     return dq, dk, dv

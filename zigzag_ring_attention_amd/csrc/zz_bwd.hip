@@ -33,18 +33,19 @@ struct BwdArgs {
     int64_t T;
     int32_t n, hq, hkv;
     float scale, scale_log2;
+    int32_t accumulate;
 };
 
 // Read-add-write of a lane's column of a transposed accumulator (C layout:
 // register i of block b is element 32*b + c_row(i, l/32) of the row).
 template <int NB>
-__device__ __forceinline__ void add_row(float *row, const f32x16 (&acc)[NB], float mul, int hh) {
+__device__ __forceinline__ void add_row(float *row, const f32x16 (&acc)[NB], float mul, int hh, bool accumulate) {
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
             float4 *dst = reinterpret_cast<float4 *>(row + 32 * b + c_row(4 * i4, hh));
-            float4 o = *dst;
+            float4 o = accumulate ? *dst : float4{0.f, 0.f, 0.f, 0.f};
             o.x += acc[b][4 * i4 + 0] * mul;
             o.y += acc[b][4 * i4 + 1] * mul;
             o.z += acc[b][4 * i4 + 2] * mul;
@@ -94,44 +95,61 @@ bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) dk[b][i] = dv[b][i] = 0.0f;
 
-    for (int h = kvh * G; h < (kvh + 1) * G; ++h) {
-        for (int t = it.tbeg; t < it.tend; ++t) {
-            const TileRec tr = a.tiles[t];
-            const int nq = tr.b1 - tr.b0;
-            __syncthreads();
-            load_tile<T, D, kThreads>(Qs, q, qrow0 + tr.b0, nq, kQT, a.hq, h, tid);
-            load_tile<T, D, kThreads>(Ds, dout, qrow0 + tr.b0, nq, kQT, a.hq, h, tid);
-            if (tid < kQT) {
-                const bool ok = tid < nq;
-                lse_s[tid] = ok ? a.lse[(int64_t)h * a.T + qrow0 + tr.b0 + tid] * kLog2e : 0.0f;
-                dlt_s[tid] = ok ? a.delta[(int64_t)h * a.T + qrow0 + tr.b0 + tid] : 0.0f;
+    // Walk (query head of the group) x (listed query tile) as one sequence so
+    // the next tile's loads are always in flight during the current compute.
+    const int ntile = it.tend - it.tbeg;
+    const int nwork = G * ntile;
+    TileStage<T, D, kQT, kThreads> qst, dst;
+    float lse_r = 0.0f, dlt_r = 0.0f;
+    auto fetch = [&](int u) {
+        const int h = kvh * G + u / ntile;
+        const TileRec tn = a.tiles[it.tbeg + u % ntile];
+        const int nq = tn.b1 - tn.b0;
+        qst.load(q, qrow0 + tn.b0, nq, a.hq, h, tid);
+        dst.load(dout, qrow0 + tn.b0, nq, a.hq, h, tid);
+        if (tid < kQT) {
+            const bool ok = tid < nq;
+            lse_r = ok ? a.lse[(int64_t)h * a.T + qrow0 + tn.b0 + tid] * kLog2e : 0.0f;
+            dlt_r = ok ? a.delta[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : 0.0f;
+        }
+    };
+    fetch(0);
+    for (int u = 0; u < nwork; ++u) {
+        const TileRec tr = a.tiles[it.tbeg + u % ntile];
+        const int nq = tr.b1 - tr.b0;
+        __syncthreads();
+        qst.store(Qs, tid);
+        dst.store(Ds, tid);
+        if (tid < kQT) {
+            lse_s[tid] = lse_r;
+            dlt_s[tid] = dlt_r;
+        }
+        __syncthreads();
+        if (u + 1 < nwork) fetch(u + 1);
+        if (!wave_on) continue;
+#pragma unroll
+        for (int qb = 0; qb < kQT / 32; ++qb) {
+            if (qb * 32 >= nq) break;
+            f32x16 s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+            M::gemm_rows_lds(s, Qs + (qb * 32 + (lane & 31)) * LD, kop, hh);
+            M::gemm_rows_lds(dp, Ds + (qb * 32 + (lane & 31)) * LD, vop, hh);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int qq = qb * 32 + c_row(i, hh);
+                const bool vis = qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk);
+                const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse_s[qq])) : 0.0f;
+                s[i] = p;
+                dp[i] = p * (dp[i] - dlt_s[qq]);
             }
-            __syncthreads();
-            if (!wave_on) continue;
-#pragma unroll
-            for (int qb = 0; qb < kQT / 32; ++qb) {
-                if (qb * 32 >= nq) break;
-                f32x16 s, dp;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
-                M::gemm_rows_lds(s, Qs + (qb * 32 + (lane & 31)) * LD, kop, hh);
-                M::gemm_rows_lds(dp, Ds + (qb * 32 + (lane & 31)) * LD, vop, hh);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int qq = qb * 32 + c_row(i, hh);
-                    const bool vis = qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk);
-                    const float p = vis ? __builtin_amdgcn_exp2f(s[i] * a.scale_log2 - lse_s[qq]) : 0.0f;
-                    s[i] = p;
-                    dp[i] = p * (dp[i] - dlt_s[qq]);
-                }
-                M::gemm_tr_c(dv, Ds, qb * 32, s, lane);
-                M::gemm_tr_c(dk, Qs, qb * 32, dp, lane);
-            }
+            M::gemm_tr_c(dv, Ds, qb * 32, s, lane);
+            M::gemm_tr_c(dk, Qs, qb * 32, dp, lane);
         }
     }
     if (!key_ok) return;
-    add_row<NB>(a.dk + (krow * a.hkv + kvh) * D, dk, a.scale, hh);
-    add_row<NB>(a.dv + (krow * a.hkv + kvh) * D, dv, 1.0f, hh);
+    add_row<NB>(a.dk + (krow * a.hkv + kvh) * D, dk, a.scale, hh, a.accumulate != 0);
+    add_row<NB>(a.dv + (krow * a.hkv + kvh) * D, dv, 1.0f, hh, a.accumulate != 0);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -177,13 +195,24 @@ bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
+    TileStage<T, D, kKT, kThreads> kst, vst;
+    {
+        const TileRec tr0 = a.tiles[it.tbeg];
+        kst.load(k, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
+        vst.load(v, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
+    }
     for (int t = it.tbeg; t < it.tend; ++t) {
         const TileRec tr = a.tiles[t];
         const int nk = tr.b1 - tr.b0;
         __syncthreads();
-        load_tile<T, D, kThreads>(Ks, k, kv_row0 + tr.b0, nk, kKT, a.hkv, kvh, tid);
-        load_tile<T, D, kThreads>(Vs, v, kv_row0 + tr.b0, nk, kKT, a.hkv, kvh, tid);
+        kst.store(Ks, tid);
+        vst.store(Vs, tid);
         __syncthreads();
+        if (t + 1 < it.tend) {
+            const TileRec tn = a.tiles[t + 1];
+            kst.load(k, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
+            vst.load(v, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
+        }
         if (!wave_on) continue;
 #pragma unroll
         for (int kb = 0; kb < kKT / 32; ++kb) {
@@ -197,27 +226,27 @@ bwd_dq_kernel(BwdArgs a) {
             for (int i = 0; i < 16; ++i) {
                 const int kk = kb * 32 + c_row(i, hh);
                 const bool vis = kk < nk && row_ok && tile_visible(tr.kind, tr.delta, qq, kk);
-                const float p = vis ? __builtin_amdgcn_exp2f(s[i] * a.scale_log2 - lse2) : 0.0f;
+                const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2)) : 0.0f;
                 dp[i] = p * (dp[i] - dlt);
             }
             M::gemm_tr_c(acc, Ks, kb * 32, dp, lane);
         }
     }
     if (!row_ok) return;
-    add_row<NB>(a.dq + (zrow * a.hq + head) * D, acc, a.scale, hh);
+    add_row<NB>(a.dq + (zrow * a.hq + head) * D, acc, a.scale, hh, a.accumulate != 0);
 }
 
 template <typename T, int D>
-hipError_t launch_t(const zz_plan *p, int rank, int step, BwdArgs a, hipStream_t st) {
+hipError_t launch_t(const zz_plan *p, int rank, int step, BwdArgs a, int which, hipStream_t st) {
     const Launch Lkv = launch_items(p, ZZ_PASS_BWD_DKV, rank, step);
-    if (Lkv.n > 0) {
+    if ((which & 1) && Lkv.n > 0) {
         a.items = Lkv.items; a.order = Lkv.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DKV);
         hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), dim3(Lkv.n, p->hkv), dim3(kThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const Launch Lq = launch_items(p, ZZ_PASS_BWD_DQ, rank, step);
-    if (Lq.n > 0) {
+    if ((which & 2) && Lq.n > 0) {
         a.items = Lq.items; a.order = Lq.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DQ);
         hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(Lq.n, p->hq), dim3(kThreads), 0, st, a);
     }
@@ -228,7 +257,7 @@ hipError_t launch_t(const zz_plan *p, int rank, int step, BwdArgs a, hipStream_t
 
 hipError_t launch_bwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k, const void *v,
                            const void *dout, const float *lse, const float *delta, float *dq, float *dk,
-                           float *dv, hipStream_t st) {
+                           float *dv, int accumulate, int which, hipStream_t st) {
     BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = delta;
     a.dq = dq; a.dk = dk; a.dv = dv;
@@ -236,14 +265,15 @@ hipError_t launch_bwd_step(const zz_plan *p, int rank, int step, const void *q, 
     a.T = p->T; a.n = (int32_t)(p->T / p->cp); a.hq = p->hq; a.hkv = p->hkv;
     a.scale = (float)(1.0 / std::sqrt((double)p->d));
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
+    a.accumulate = accumulate;
     if (p->dtype == ZZ_BF16) {
-        if (p->d == 32) return launch_t<bf16, 32>(p, rank, step, a, st);
-        if (p->d == 64) return launch_t<bf16, 64>(p, rank, step, a, st);
-        return launch_t<bf16, 128>(p, rank, step, a, st);
+        if (p->d == 32) return launch_t<bf16, 32>(p, rank, step, a, which, st);
+        if (p->d == 64) return launch_t<bf16, 64>(p, rank, step, a, which, st);
+        return launch_t<bf16, 128>(p, rank, step, a, which, st);
     }
-    if (p->d == 32) return launch_t<float, 32>(p, rank, step, a, st);
-    if (p->d == 64) return launch_t<float, 64>(p, rank, step, a, st);
-    return launch_t<float, 128>(p, rank, step, a, st);
+    if (p->d == 32) return launch_t<float, 32>(p, rank, step, a, which, st);
+    if (p->d == 64) return launch_t<float, 64>(p, rank, step, a, which, st);
+    return launch_t<float, 128>(p, rank, step, a, which, st);
 }
 
 }  // namespace zz

@@ -240,12 +240,40 @@ zz_status zz_bwd_preprocess(const zz_plan *p, const void *o_zz, const void *do_z
 zz_status zz_varlen_ring_step_bwd(const zz_plan *p, int32_t rank, int32_t step, const void *q_zz,
                                   const void *k_zz, const void *v_zz, const void *do_zz,
                                   const float *lse, const float *delta, float *dq_acc,
-                                  float *dk_acc, float *dv_acc, void *stream) {
+                                  float *dk_acc, float *dv_acc, int32_t accumulate, void *stream) {
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_rank_step(p, rank, step, true));
     ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc, dk_acc, dv_acc}));
+    if (accumulate != 0 && accumulate != 1) return fail(ZZ_ERR_ARG, "accumulate must be 0 or 1");
     return hip_status(zz::launch_bwd_step(p, rank, step, q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc,
-                                          dk_acc, dv_acc, (hipStream_t)stream), "varlen_ring_step_bwd");
+                                          dk_acc, dv_acc, accumulate, 3, (hipStream_t)stream),
+                      "varlen_ring_step_bwd");
+}
+
+zz_status zz_varlen_ring_step_bwd_dkv(const zz_plan *p, int32_t rank, int32_t step, const void *q_zz,
+                                      const void *k_zz, const void *v_zz, const void *do_zz,
+                                      const float *lse, const float *delta, float *dk_acc,
+                                      float *dv_acc, int32_t accumulate, void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_rank_step(p, rank, step, true));
+    ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dk_acc, dv_acc}));
+    if (accumulate != 0 && accumulate != 1) return fail(ZZ_ERR_ARG, "accumulate must be 0 or 1");
+    return hip_status(zz::launch_bwd_step(p, rank, step, q_zz, k_zz, v_zz, do_zz, lse, delta, nullptr,
+                                          dk_acc, dv_acc, accumulate, 1, (hipStream_t)stream),
+                      "varlen_ring_step_bwd_dkv");
+}
+
+zz_status zz_varlen_ring_step_bwd_dq(const zz_plan *p, int32_t rank, int32_t step, const void *q_zz,
+                                     const void *k_zz, const void *v_zz, const void *do_zz,
+                                     const float *lse, const float *delta, float *dq_acc,
+                                     int32_t accumulate, void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_rank_step(p, rank, step, true));
+    ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc}));
+    if (accumulate != 0 && accumulate != 1) return fail(ZZ_ERR_ARG, "accumulate must be 0 or 1");
+    return hip_status(zz::launch_bwd_step(p, rank, step, q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc,
+                                          nullptr, nullptr, accumulate, 2, (hipStream_t)stream),
+                      "varlen_ring_step_bwd_dq");
 }
 
 zz_status zz_finalize_bwd(const zz_plan *p, const float *dq_acc, const float *dk_acc,

@@ -82,18 +82,32 @@ fwd_step_kernel(FwdArgs a) {
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
-    // lsum: sum of the weights as rounded for the P.V product (normalizes O);
-    // lexp: sum of the unrounded weights (gives the LSE).
-    float m = -INFINITY, lsum = 0.0f, lexp = 0.0f;
+    // m: reference maximum of the scaled scores (log2 units) that every weight
+    // of this query is taken relative to.  It is only moved when a tile's
+    // maximum exceeds it by more than kLazy, so weights stay below 2^kLazy and
+    // the O rescale is skipped on most tiles.
+    constexpr float kLazy = 8.0f;
+    float m = -INFINITY, lsum = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
+    TileStage<T, D, kBN, kThreads> kst, vst;
+    {
+        const TileRec tr0 = a.tiles[it.tbeg];
+        kst.load(k, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
+        vst.load(v, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
+    }
     for (int t = it.tbeg; t < it.tend; ++t) {
         const TileRec tr = a.tiles[t];
         const int nk = tr.b1 - tr.b0;
+        __syncthreads();             // every wave is done with the previous tile
+        kst.store(Ks, tid);
+        vst.store(Vs, tid);
         __syncthreads();
-        load_tile<T, D, kThreads>(Ks, k, kv_row0 + tr.b0, nk, kBN, a.hkv, kvh, tid);
-        load_tile<T, D, kThreads>(Vs, v, kv_row0 + tr.b0, nk, kBN, a.hkv, kvh, tid);
-        __syncthreads();
+        if (t + 1 < it.tend) {       // prefetch the next tile while this one is computed
+            const TileRec tn = a.tiles[t + 1];
+            kst.load(k, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
+            vst.load(v, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
+        }
         if (!wave_on) continue;
 
         f32x16 s[2];
@@ -103,43 +117,45 @@ fwd_step_kernel(FwdArgs a) {
             for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
             if (kb == 0 || nk > 32) M::gemm_rows_lds(s[kb], Ks + (kb * 32 + (lane & 31)) * LD, qop, hh);
         }
-        // scale, mask, block max
-        const bool need_mask = tr.kind != ZZ_TILE_FULL || nk < kBN;
-        float mt = -INFINITY;
+        // mask (partial and ragged tiles only), raw block maximum
+        if (tr.kind != ZZ_TILE_FULL || nk < kBN) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = s[kb][i] * a.scale_log2;
-                if (need_mask) {
+                for (int i = 0; i < 16; ++i) {
                     const int kk = kb * 32 + c_row(i, hh);
-                    if (kk >= nk || !tile_visible(tr.kind, tr.delta, qq, kk)) x = -INFINITY;
+                    if (kk >= nk || !tile_visible(tr.kind, tr.delta, qq, kk)) s[kb][i] = -INFINITY;
                 }
-                s[kb][i] = x;
-                mt = fmaxf(mt, x);
-            }
-        mt = fmaxf(mt, swap_halves(mt, lane));
-        const float mnew = fmaxf(m, mt);
+        }
+        float mraw = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[kb][i]);
+        mraw = fmaxf(mraw, swap_halves(mraw, lane));
+        const float mt = mraw * a.scale_log2;     // scale > 0 commutes with max
+        const bool move = mt > m + kLazy;         // false for an all-masked tile
+        const float mnew = move ? mt : m;
         const float msafe = mnew == -INFINITY ? 0.0f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-        float ps = 0.0f, pe = 0.0f;
+        if (__builtin_amdgcn_ballot_w64(move)) {
+            const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+            lsum *= alpha;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+        }
+        m = mnew;
+        float ps = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float e = __builtin_amdgcn_exp2f(s[kb][i] - msafe);
-                const float p = M::round_p(e);
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -msafe));
                 s[kb][i] = p;
                 ps += p;
-                pe += e;
             }
-        lsum = lsum * alpha + ps;
-        lexp = lexp * alpha + pe;
-        m = mnew;
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+        lsum += ps;
         M::gemm_tr_c(acc, Vs, 0, s[0], lane);
         if (nk > 32) M::gemm_tr_c(acc, Vs, 32, s[1], lane);
     }
@@ -147,9 +163,8 @@ fwd_step_kernel(FwdArgs a) {
 
     // Epilogue: the lane pair (l, l^32) holds one query's keys split in two.
     const float ltot = lsum + swap_halves(lsum, lane);
-    const float etot = lexp + swap_halves(lexp, lane);
     const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-    const float lse_b = etot > 0.0f ? (m + log2f(etot)) * 0.69314718055994530942f : -INFINITY;
+    const float lse_b = ltot > 0.0f ? (m + log2f(ltot)) * 0.69314718055994530942f : -INFINITY;
     float *orow = a.o + (zrow * a.hq + head) * D;
     float *lse_p = a.lse + (int64_t)head * a.T + zrow;
     if (!a.merge) {

@@ -105,8 +105,9 @@ hipError_t launch_debug_mask(const zz_plan *p, int pass, int rank, int step, uin
                              hipStream_t st);
 hipError_t launch_fwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k,
                            const void *v, float *o, float *lse, int merge, hipStream_t st);
+// which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.
 hipError_t launch_bwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k,
                            const void *v, const void *dout, const float *lse, const float *delta,
-                           float *dq, float *dk, float *dv, hipStream_t st);
+                           float *dq, float *dk, float *dv, int accumulate, int which, hipStream_t st);
 
 }  // namespace zz

@@ -43,10 +43,6 @@ template <int D> struct Mfma<bf16, D> {
     static constexpr int LD = D + PAD;  // LDS row stride (elements)
     typedef bf16x8 Op;
 
-    // Softmax weights enter the P.V product rounded to bf16; the row sum uses
-    // the same rounded values so that the weights stay normalized.
-    static __device__ __forceinline__ float round_p(float p) { return static_cast<float>(to_bf16(p)); }
-
     // Row-major operand of one lane: 8 consecutive values at column 16*ks + 8*hh.
     static __device__ __forceinline__ void load_row_op(Op (&op)[KS], const bf16 *row, int hh) {
 #pragma unroll
@@ -113,8 +109,6 @@ template <int D> struct Mfma<float, D> {
     static constexpr int LD = D + PAD;
     typedef float Op;
 
-    static __device__ __forceinline__ float round_p(float p) { return p; }
-
     static __device__ __forceinline__ void load_row_op(Op (&op)[KS], const float *row, int hh) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) op[ks] = row[2 * ks + hh];
@@ -142,20 +136,34 @@ template <int D> struct Mfma<float, D> {
     }
 };
 
-// Cooperative copy of rows [r0, r0 + nrows) of a [*, H, D] tensor (head h) into
-// a padded LDS tile of `cap` rows; rows past nrows are zero-filled.
-template <typename T, int D, int NT>
-__device__ __forceinline__ void load_tile(T *lds, const T *__restrict__ g, int64_t row0, int nrows, int cap,
-                                          int heads, int h, int tid) {
-    constexpr int EPV = 16 / sizeof(T);
-    constexpr int CPR = D / EPV;   // 16-byte chunks per row
-    constexpr int LD = Mfma<T, D>::LD;
-    for (int c = tid; c < cap * CPR; c += NT) {
-        const int r = c / CPR, e = (c % CPR) * EPV;
-        int4 v = {0, 0, 0, 0};
-        if (r < nrows) v = *reinterpret_cast<const int4 *>(g + ((row0 + r) * heads + h) * D + e);
-        *reinterpret_cast<int4 *>(lds + r * LD + e) = v;
+// A tile of ROWS rows x D columns of a [*, H, D] tensor (one head), staged
+// global -> registers -> LDS by NT threads.  Issuing the global loads for the
+// next tile before computing on the current one hides their latency.
+// Rows past nrows are zero-filled (no read past the end of a chunk).
+template <typename T, int D, int ROWS, int NT> struct TileStage {
+    static constexpr int EPV = 16 / sizeof(T);   // elements per 16-byte chunk
+    static constexpr int CPR = D / EPV;          // chunks per row
+    static constexpr int N = ROWS * CPR / NT;    // chunks per thread
+    static_assert(N >= 1 && (ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
+    static constexpr int LD = Mfma<T, D>::LD;
+    int4 r[N];
+
+    __device__ __forceinline__ void load(const T *__restrict__ g, int64_t row0, int nrows, int heads, int h,
+                                         int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int c = tid + i * NT, row = c / CPR, e = (c % CPR) * EPV;
+            r[i] = row < nrows ? *reinterpret_cast<const int4 *>(g + ((row0 + row) * heads + h) * D + e)
+                               : int4{0, 0, 0, 0};
+        }
     }
-}
+    __device__ __forceinline__ void store(T *lds, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int c = tid + i * NT, row = c / CPR, e = (c % CPR) * EPV;
+            *reinterpret_cast<int4 *>(lds + row * LD + e) = r[i];
+        }
+    }
+};
 
 }  // namespace zz
