@@ -30,7 +30,8 @@ ALL_STEPS = -1
 F32, BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libzz.so")
+# ZZ_LIBRARY may point at another build of libzz (e.g. a tuning variant).
+_LIB_PATH = os.environ.get("ZZ_LIBRARY") or os.path.join(_HERE, "libzz.so")
 _lib = None
 
 

@@ -17,6 +17,14 @@
 
 #include "zz_mfma.h"
 
+// Waves per SIMD each kernel is compiled for (register budget 512 / waves).
+#ifndef ZZ_DKV_WAVES
+#define ZZ_DKV_WAVES 1
+#endif
+#ifndef ZZ_DQ_WAVES
+#define ZZ_DQ_WAVES 2
+#endif
+
 namespace zz {
 namespace {
 
@@ -56,17 +64,31 @@ __device__ __forceinline__ void add_row(float *row, const f32x16 (&acc)[NB], flo
 
 // ---------------------------------------------------------------- dK, dV
 
-constexpr int kQT = 64;   // query rows per streamed tile
+// Query rows per streamed tile (must match the planner's dK/dV tile).
+template <typename T, int D> constexpr int q_tile() { return (sizeof(T) == 4 && D == 128) ? 32 : 64; }
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_DKV_WAVES)))
 bwd_dkv_kernel(BwdArgs a) {
+    constexpr int kQT = q_tile<T, D>();
     using M = Mfma<T, D>;
+    using TStage = TileStageT<T, D, kQT, kThreads>;
     constexpr int LD = M::LD;
+    constexpr int LDT = TStage::LDT;
     constexpr int NB = D / 32;
-    __shared__ __attribute__((aligned(16))) T Qs[kQT * LD];
-    __shared__ __attribute__((aligned(16))) T Ds[kQT * LD];
-    __shared__ float lse_s[kQT], dlt_s[kQT];
+    // Q and dO of the current (head, query tile), each twice: row-major for
+    // S = Q K^T and dP = dO V^T (A operands with the head dim contiguous), and
+    // transposed for dK^T += Q^T dS and dV^T += dO^T P (A operands with the
+    // queries contiguous), so every operand read is a 16-byte LDS read.
+    // Double-buffered: the next tile is loaded into registers during the
+    // current compute and stored to the other buffer; one barrier per tile.
+    // The key-side operands and the dK/dV accumulators stay in registers for
+    // the whole item, which costs the second wave per SIMD.
+    __shared__ __attribute__((aligned(16))) T Qs[2][kQT * LD];
+    __shared__ __attribute__((aligned(16))) T Ds[2][kQT * LD];
+    __shared__ __attribute__((aligned(16))) T QsT[2][D * LDT];
+    __shared__ __attribute__((aligned(16))) T DsT[2][D * LDT];
+    __shared__ float lse_s[2][kQT], dlt_s[2][kQT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
     const int kvh = blockIdx.y;
@@ -95,57 +117,67 @@ bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) dk[b][i] = dv[b][i] = 0.0f;
 
-    // Walk (query head of the group) x (listed query tile) as one sequence so
-    // the next tile's loads are always in flight during the current compute.
+    // Walk (query head of the group) x (listed query tile) as one sequence.
     const int ntile = it.tend - it.tbeg;
     const int nwork = G * ntile;
-    TileStage<T, D, kQT, kThreads> qst, dst;
+    TStage qt, dt;   // one load each feeds both the row-major and the transposed copy
     float lse_r = 0.0f, dlt_r = 0.0f;
     auto fetch = [&](int u) {
         const int h = kvh * G + u / ntile;
         const TileRec tn = a.tiles[it.tbeg + u % ntile];
         const int nq = tn.b1 - tn.b0;
-        qst.load(q, qrow0 + tn.b0, nq, a.hq, h, tid);
-        dst.load(dout, qrow0 + tn.b0, nq, a.hq, h, tid);
+        qt.load(q, qrow0 + tn.b0, nq, a.hq, h, tid);
+        dt.load(dout, qrow0 + tn.b0, nq, a.hq, h, tid);
         if (tid < kQT) {
             const bool ok = tid < nq;
             lse_r = ok ? a.lse[(int64_t)h * a.T + qrow0 + tn.b0 + tid] * kLog2e : 0.0f;
             dlt_r = ok ? a.delta[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : 0.0f;
         }
     };
+    auto stash = [&](int buf) {
+        qt.store_rows(Qs[buf], tid);
+        dt.store_rows(Ds[buf], tid);
+        qt.store(QsT[buf], tid);
+        dt.store(DsT[buf], tid);
+        if (tid < kQT) {
+            lse_s[buf][tid] = lse_r;
+            dlt_s[buf][tid] = dlt_r;
+        }
+    };
     fetch(0);
+    stash(0);
+    __syncthreads();
     for (int u = 0; u < nwork; ++u) {
+        const int buf = u & 1;
         const TileRec tr = a.tiles[it.tbeg + u % ntile];
         const int nq = tr.b1 - tr.b0;
-        __syncthreads();
-        qst.store(Qs, tid);
-        dst.store(Ds, tid);
-        if (tid < kQT) {
-            lse_s[tid] = lse_r;
-            dlt_s[tid] = dlt_r;
-        }
-        __syncthreads();
-        if (u + 1 < nwork) fetch(u + 1);
-        if (!wave_on) continue;
+        const bool more = u + 1 < nwork;
+        if (more) fetch(u + 1);
+        if (wave_on) {
+            const T *qs = Qs[buf], *ds = Ds[buf], *qst = QsT[buf], *dst = DsT[buf];
+            const float *ls = lse_s[buf], *dl = dlt_s[buf];
 #pragma unroll
-        for (int qb = 0; qb < kQT / 32; ++qb) {
-            if (qb * 32 >= nq) break;
-            f32x16 s, dp;
+            for (int qb = 0; qb < kQT / 32; ++qb) {
+                if (qb * 32 >= nq) break;
+                f32x16 s, dp;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
-            M::gemm_rows_lds(s, Qs + (qb * 32 + (lane & 31)) * LD, kop, hh);
-            M::gemm_rows_lds(dp, Ds + (qb * 32 + (lane & 31)) * LD, vop, hh);
+                for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+                M::gemm_rows_lds(s, qs, qb * 32 + (lane & 31), kop, hh);
+                M::gemm_rows_lds(dp, ds, qb * 32 + (lane & 31), vop, hh);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int qq = qb * 32 + c_row(i, hh);
-                const bool vis = qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk);
-                const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse_s[qq])) : 0.0f;
-                s[i] = p;
-                dp[i] = p * (dp[i] - dlt_s[qq]);
+                for (int i = 0; i < 16; ++i) {
+                    const int qq = qb * 32 + c_row(i, hh);
+                    const bool vis = qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk);
+                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -ls[qq])) : 0.0f;
+                    s[i] = p;
+                    dp[i] = p * (dp[i] - dl[qq]);
+                }
+                M::template gemm_t_c<LDT>(dv, dst, qb * 32, s, lane);
+                M::template gemm_t_c<LDT>(dk, qst, qb * 32, dp, lane);
             }
-            M::gemm_tr_c(dv, Ds, qb * 32, s, lane);
-            M::gemm_tr_c(dk, Qs, qb * 32, dp, lane);
         }
+        if (more) stash(buf ^ 1);
+        __syncthreads();
     }
     if (!key_ok) return;
     add_row<NB>(a.dk + (krow * a.hkv + kvh) * D, dk, a.scale, hh, a.accumulate != 0);
@@ -157,12 +189,18 @@ bwd_dkv_kernel(BwdArgs a) {
 constexpr int kKT = 64;   // keys per streamed tile
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_DQ_WAVES)))
 bwd_dq_kernel(BwdArgs a) {
     using M = Mfma<T, D>;
+    using RStage = TileStage<T, D, kKT, kThreads>;
+    using TStage = TileStageT<T, D, kKT, kThreads>;
     constexpr int LD = M::LD;
+    constexpr int LDT = TStage::LDT;
     constexpr int NB = D / 32;
+    // K row-major (S^T = K Q^T), K transposed (dQ^T += K^T dS^T), V row-major
+    // (dP^T = V dO^T).
     __shared__ __attribute__((aligned(16))) T Ks[kKT * LD];
+    __shared__ __attribute__((aligned(16))) T KsT[D * LDT];
     __shared__ __attribute__((aligned(16))) T Vs[kKT * LD];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
@@ -195,22 +233,24 @@ bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
-    TileStage<T, D, kKT, kThreads> kst, vst;
+    RStage vst;
+    TStage ktst;   // one load of K feeds both its row-major and transposed copies
     {
         const TileRec tr0 = a.tiles[it.tbeg];
-        kst.load(k, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
+        ktst.load(k, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
         vst.load(v, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
     }
     for (int t = it.tbeg; t < it.tend; ++t) {
         const TileRec tr = a.tiles[t];
         const int nk = tr.b1 - tr.b0;
         __syncthreads();
-        kst.store(Ks, tid);
+        ktst.store_rows(Ks, tid);
+        ktst.store(KsT, tid);
         vst.store(Vs, tid);
         __syncthreads();
-        if (t + 1 < it.tend) {
+        if (t + 1 < it.tend) {       // next tile's loads fly during this compute
             const TileRec tn = a.tiles[t + 1];
-            kst.load(k, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
+            ktst.load(k, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
             vst.load(v, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
         }
         if (!wave_on) continue;
@@ -220,8 +260,8 @@ bwd_dq_kernel(BwdArgs a) {
             f32x16 s, dp;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
-            M::gemm_rows_lds(s, Ks + (kb * 32 + (lane & 31)) * LD, qop, hh);
-            M::gemm_rows_lds(dp, Vs + (kb * 32 + (lane & 31)) * LD, dop, hh);
+            M::gemm_rows_lds(s, Ks, kb * 32 + (lane & 31), qop, hh);
+            M::gemm_rows_lds(dp, Vs, kb * 32 + (lane & 31), dop, hh);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int kk = kb * 32 + c_row(i, hh);
@@ -229,7 +269,7 @@ bwd_dq_kernel(BwdArgs a) {
                 const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2)) : 0.0f;
                 dp[i] = p * (dp[i] - dlt);
             }
-            M::gemm_tr_c(acc, Ks, kb * 32, dp, lane);
+            M::template gemm_t_c<LDT>(acc, KsT, kb * 32, dp, lane);
         }
     }
     if (!row_ok) return;

@@ -20,6 +20,10 @@
 
 #include "zz_mfma.h"
 
+#ifndef ZZ_FWD_WAVES
+#define ZZ_FWD_WAVES 2
+#endif
+
 namespace zz {
 namespace {
 
@@ -42,13 +46,17 @@ struct FwdArgs {
 };
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_FWD_WAVES)))
 fwd_step_kernel(FwdArgs a) {
     using M = Mfma<T, D>;
+    using VStage = TileStageT<T, D, kBN, kThreads>;
     constexpr int LD = M::LD;
+    constexpr int LDT = VStage::LDT;
     constexpr int NB = D / 32;   // 32-wide head-dim blocks of O^T
-    __shared__ __attribute__((aligned(16))) T Ks[kBN * LD];
-    __shared__ __attribute__((aligned(16))) T Vs[kBN * LD];
+    // Double-buffered: K row-major (A operand of S^T = K Q^T), V transposed
+    // (A operand of O^T = V^T P^T).  One barrier per tile.
+    __shared__ __attribute__((aligned(16))) T Ks[2][kBN * LD];
+    __shared__ __attribute__((aligned(16))) T Vt[2][D * LDT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
     const int head = blockIdx.y;
@@ -90,74 +98,83 @@ fwd_step_kernel(FwdArgs a) {
     float m = -INFINITY, lsum = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
-    TileStage<T, D, kBN, kThreads> kst, vst;
+    TileStage<T, D, kBN, kThreads> kst;
+    VStage vst;
     {
         const TileRec tr0 = a.tiles[it.tbeg];
         kst.load(k, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
         vst.load(v, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
+        kst.store(Ks[0], tid);
+        vst.store(Vt[0], tid);
     }
+    __syncthreads();
     for (int t = it.tbeg; t < it.tend; ++t) {
+        const int buf = (t - it.tbeg) & 1;
         const TileRec tr = a.tiles[t];
         const int nk = tr.b1 - tr.b0;
-        __syncthreads();             // every wave is done with the previous tile
-        kst.store(Ks, tid);
-        vst.store(Vs, tid);
-        __syncthreads();
-        if (t + 1 < it.tend) {       // prefetch the next tile while this one is computed
+        const bool more = t + 1 < it.tend;
+        if (more) {                  // next tile's loads fly while this one is computed
             const TileRec tn = a.tiles[t + 1];
             kst.load(k, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
             vst.load(v, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
         }
-        if (!wave_on) continue;
-
-        f32x16 s[2];
+        if (wave_on) {
+            const T *ks = Ks[buf];
+            const T *vt = Vt[buf];
+            f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-            if (kb == 0 || nk > 32) M::gemm_rows_lds(s[kb], Ks + (kb * 32 + (lane & 31)) * LD, qop, hh);
-        }
-        // mask (partial and ragged tiles only), raw block maximum
-        if (tr.kind != ZZ_TILE_FULL || nk < kBN) {
+                for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
+                if (kb == 0 || nk > 32) M::gemm_rows_lds(s[kb], ks, kb * 32 + (lane & 31), qop, hh);
+            }
+            // mask (partial and ragged tiles only), raw block maximum
+            if (tr.kind != ZZ_TILE_FULL || nk < kBN) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int kk = kb * 32 + c_row(i, hh);
+                        if (kk >= nk || !tile_visible(tr.kind, tr.delta, qq, kk)) s[kb][i] = -INFINITY;
+                    }
+            }
+            float mraw = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[kb][i]);
+            mraw = fmaxf(mraw, swap_halves(mraw, lane));
+            const float mt = mraw * a.scale_log2;     // scale > 0 commutes with max
+            const bool move = mt > m + kLazy;         // false for an all-masked tile
+            const float mnew = move ? mt : m;
+            const float msafe = mnew == -INFINITY ? 0.0f : mnew;
+            if (__builtin_amdgcn_ballot_w64(move)) {
+                const float alpha = __builtin_amdgcn_exp2f(m - msafe);
+                lsum *= alpha;
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+            }
+            m = mnew;
+            float ps = 0.0f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int kk = kb * 32 + c_row(i, hh);
-                    if (kk >= nk || !tile_visible(tr.kind, tr.delta, qq, kk)) s[kb][i] = -INFINITY;
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -msafe));
+                    s[kb][i] = p;
+                    ps += p;
                 }
+            lsum += ps;
+            M::template gemm_t_c<LDT>(acc, vt, 0, s[0], lane);
+            if (nk > 32) M::template gemm_t_c<LDT>(acc, vt, 32, s[1], lane);
         }
-        float mraw = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[kb][i]);
-        mraw = fmaxf(mraw, swap_halves(mraw, lane));
-        const float mt = mraw * a.scale_log2;     // scale > 0 commutes with max
-        const bool move = mt > m + kLazy;         // false for an all-masked tile
-        const float mnew = move ? mt : m;
-        const float msafe = mnew == -INFINITY ? 0.0f : mnew;
-        if (__builtin_amdgcn_ballot_w64(move)) {
-            const float alpha = __builtin_amdgcn_exp2f(m - msafe);
-            lsum *= alpha;
-#pragma unroll
-            for (int b = 0; b < NB; ++b)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+        if (more) {
+            kst.store(Ks[buf ^ 1], tid);
+            vst.store(Vt[buf ^ 1], tid);
         }
-        m = mnew;
-        float ps = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][i], a.scale_log2, -msafe));
-                s[kb][i] = p;
-                ps += p;
-            }
-        lsum += ps;
-        M::gemm_tr_c(acc, Vs, 0, s[0], lane);
-        if (nk > 32) M::gemm_tr_c(acc, Vs, 32, s[1], lane);
+        __syncthreads();
     }
     if (!row_ok) return;
 

@@ -5,28 +5,27 @@
 //    e = 0..7; B[k][n] in lane (n = l%32), k = 8*(l/32) + e; C[m][n] in lane
 //    (n = l%32), register i holds m = 8*(i/4) + 4*(l/32) + i%4.
 //  v_mfma_f32_32x32x2_f32: as above with one k per lane, k = l/32.
-//  ds_read_b64_tr_b16: in each group of 16 lanes, lane t supplies the address
-//    of 4 consecutive 16-bit values; lane t of the group then receives the
-//    values at positions t, 16+t, 32+t, 48+t of the 64 values the group
-//    loaded (in lane order).  Pointing lane t at row (k0 + t/4), column
-//    (n0 + 4*(t%4)) of a row-major tile therefore hands lane t the column
-//    n0 + t, rows k0..k0+3: a transposed operand read.
 //
 // Scores are formed transposed (S^T = K Q^T), so the C layout puts one query
 // per lane column: the softmax row statistics of a query live in one lane
 // pair (l, l^32), and P^T in C layout is already the B operand of O^T = V^T P^T
 // when the contraction runs over the keys in the order k(e) = 8*(e/4) +
-// 4*(l/32) + e%4 -- the A operand (V^T) is then read with that same order.
+// 4*(l/32) + e%4 -- the A operand (V^T) is then read from a transposed LDS
+// copy whose rows hold the keys in that order (tperm).
 #pragma once
 
 #include "zz_device.h"
 
 namespace zz {
 
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
 // Key offset (inside a 32-key score block) of C register i in lane half hh.
 __device__ __forceinline__ constexpr int c_row(int i, int hh) { return 8 * (i / 4) + 4 * hh + (i % 4); }
+
+// Position of row k of a tile inside a transposed LDS row: bits 2 and 3 of k
+// swapped.  With it, the 8 contraction values a lane half needs for one
+// 32x32x16 MFMA (rows 4h..4h+3 and 8+4h..8+4h+3 of a 16-row block, the order
+// c_row produces) sit in 16 contiguous bytes.
+__device__ __forceinline__ constexpr int tperm(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
 // Exchange a value with lane l^32.
 __device__ __forceinline__ float swap_halves(float x, int lane) {
@@ -37,10 +36,19 @@ __device__ __forceinline__ float swap_halves(float x, int lane) {
 template <typename T, int D> struct Mfma;
 
 // bf16 operands, v_mfma_f32_32x32x16_bf16.
+// Row-major LDS tiles: 16 bytes of padding per row, so the 16 rows read by
+// 16 lanes (one row per lane, same column) start on 16 different bank
+// groups.
+template <typename T, int D> struct RowLayout {
+    static constexpr int EPV = 16 / sizeof(T);
+    static constexpr int LD = D + EPV;   // row stride (elements)
+    static __device__ __forceinline__ int at(int r, int e) { return r * LD + e; }
+};
+
 template <int D> struct Mfma<bf16, D> {
     static constexpr int KS = D / 16;   // contraction steps over the head dim
-    static constexpr int PAD = 8;       // LDS row padding (elements)
-    static constexpr int LD = D + PAD;  // LDS row stride (elements)
+    using RL = RowLayout<bf16, D>;
+    static constexpr int LD = RL::LD;   // row-major LDS row stride (elements)
     typedef bf16x8 Op;
 
     // Row-major operand of one lane: 8 consecutive values at column 16*ks + 8*hh.
@@ -54,40 +62,24 @@ template <int D> struct Mfma<bf16, D> {
 #pragma unroll
             for (int e = 0; e < 8; ++e) op[ks][e] = bf16(0.0f);
     }
-    // acc += A(rows of lds tile, row = row0 + l%32) x B(op), contraction over D.
-    static __device__ __forceinline__ void gemm_rows_lds(f32x16 &acc, const bf16 *lds_row, const Op (&op)[KS], int hh) {
+    // acc += A x B(op), A = row `row` of a row-major LDS tile (one row per
+    // lane: row = r0 + l%32), contraction over D.
+    static __device__ __forceinline__ void gemm_rows_lds(f32x16 &acc, const bf16 *tile, int row, const Op (&op)[KS],
+                                                         int hh) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(lds_row + 16 * ks + 8 * hh);
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row, 16 * ks + 8 * hh));
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[ks], acc, 0, 0, 0);
         }
     }
-    // Transposed read of a row-major LDS tile: lane gets column (n0 + l%16 within
-    // its 16-lane group), rows k0..k0+3, from lane-supplied addresses.
-    static __device__ __forceinline__ s16x4 tr4(const bf16 *tile, int k0, int n0, int lane) {
-        const int t = lane & 15;
-        const bf16 *p = tile + (k0 + t / 4) * LD + n0 + 4 * (t % 4);
-        return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    }
-    // A operand (8 values along the contraction) of X^T where X is a row-major
-    // LDS tile [rows][D]: lane (col = 32*cb + l%32) reads rows
-    // r0 + 4*(l/32) + {0..3} and r0 + 8 + 4*(l/32) + {0..3}.
-    static __device__ __forceinline__ bf16x8 tr_op(const bf16 *tile, int r0, int cb, int lane) {
-        const int g = lane >> 4;
-        const int n0 = 32 * cb + 16 * (g & 1);
-        const int hh = g >> 1;
-        const s16x4 x = tr4(tile, r0 + 4 * hh, n0, lane);
-        const s16x4 y = tr4(tile, r0 + 8 + 4 * hh, n0, lane);
-        // Join as whole vectors: building the result element by element through
-        // scalar 16-bit bit casts was miscompiled (lanes duplicated) by hipcc 7.2.
-        const s16x8 xy = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
-        return __builtin_bit_cast(bf16x8, xy);
-    }
-    // acc[cb] += X^T(LDS tile rows r0.. r0+31 of a 32-row block) * P where P is a
-    // 32(contraction) x 32 block in C layout (register i = contraction index
-    // c_row(i, l/32)).  Two MFMAs per 32 contraction rows.
-    static __device__ __forceinline__ void gemm_tr_c(f32x16 (&acc)[D / 32], const bf16 *tile, int r0,
-                                                     const f32x16 &p, int lane) {
+    // acc[cb] += X^T * P for a tile X stored transposed in LDS (row = column of
+    // X, LDT elements per row, X rows permuted by tperm): X rows r0..r0+31
+    // against a 32 x 32 block P in C layout.  16-byte reads, two MFMAs per
+    // 32 contraction rows and 32 columns.
+    template <int LDT>
+    static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const bf16 *tileT, int r0,
+                                                    const f32x16 &p, int lane) {
+        const int hh = lane >> 5;
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             bf16x8 b;
@@ -95,7 +87,8 @@ template <int D> struct Mfma<bf16, D> {
             for (int e = 0; e < 8; ++e) b[e] = to_bf16(p[8 * half + e]);
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb) {
-                const bf16x8 a = tr_op(tile, r0 + 16 * half, cb, lane);
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tileT + (32 * cb + (lane & 31)) * LDT + r0 +
+                                                                   16 * half + 8 * hh);
                 acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[cb], 0, 0, 0);
             }
         }
@@ -105,8 +98,8 @@ template <int D> struct Mfma<bf16, D> {
 // fp32 operands, v_mfma_f32_32x32x2_f32.
 template <int D> struct Mfma<float, D> {
     static constexpr int KS = D / 2;
-    static constexpr int PAD = 4;
-    static constexpr int LD = D + PAD;
+    using RL = RowLayout<float, D>;
+    static constexpr int LD = RL::LD;
     typedef float Op;
 
     static __device__ __forceinline__ void load_row_op(Op (&op)[KS], const float *row, int hh) {
@@ -117,20 +110,22 @@ template <int D> struct Mfma<float, D> {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) op[ks] = 0.0f;
     }
-    static __device__ __forceinline__ void gemm_rows_lds(f32x16 &acc, const float *lds_row, const Op (&op)[KS], int hh) {
+    static __device__ __forceinline__ void gemm_rows_lds(f32x16 &acc, const float *tile, int row, const Op (&op)[KS],
+                                                         int hh) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(lds_row[2 * ks + hh], op[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(tile[RL::at(row, 2 * ks + hh)], op[ks], acc, 0, 0, 0);
     }
-    static __device__ __forceinline__ void gemm_tr_c(f32x16 (&acc)[D / 32], const float *tile, int r0,
-                                                     const f32x16 &p, int lane) {
+    template <int LDT>
+    static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const float *tileT, int r0,
+                                                    const f32x16 &p, int lane) {
         const int hh = lane >> 5;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int row = r0 + c_row(i, hh);
+            const int pos = r0 + tperm(c_row(i, hh));
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(tile[row * LD + 32 * cb + (lane & 31)], p[i],
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(tileT[(32 * cb + (lane & 31)) * LDT + pos], p[i],
                                                                 acc[cb], 0, 0, 0);
         }
     }
@@ -145,8 +140,9 @@ template <typename T, int D, int ROWS, int NT> struct TileStage {
     static constexpr int CPR = D / EPV;          // chunks per row
     static constexpr int N = ROWS * CPR / NT;    // chunks per thread
     static_assert(N >= 1 && (ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
-    static constexpr int LD = Mfma<T, D>::LD;
+    static constexpr int LD = RowLayout<T, D>::LD;
     int4 r[N];
+
 
     __device__ __forceinline__ void load(const T *__restrict__ g, int64_t row0, int nrows, int heads, int h,
                                          int tid) {
@@ -162,6 +158,99 @@ template <typename T, int D, int ROWS, int NT> struct TileStage {
         for (int i = 0; i < N; ++i) {
             const int c = tid + i * NT, row = c / CPR, e = (c % CPR) * EPV;
             *reinterpret_cast<int4 *>(lds + row * LD + e) = r[i];
+        }
+    }
+};
+
+// A tile of ROWS rows x D columns of a [*, H, D] tensor (one head), staged
+// into LDS transposed: LDS row c holds column c of the tile, the tile rows
+// placed at tperm(row).  Each thread gathers 4 rows x one 16-byte column
+// group, regroups them in registers, and writes 4 consecutive rows per LDS
+// column (8 bytes for bf16, 16 for fp32).  The same registers also give the
+// row-major copy (store_rows).  Lanes are laid out as 4 column groups x 16
+// row quads x the rest of the column groups: the row-major stores of 16
+// lanes then cover 16 distinct bank groups of the padded layout.
+template <typename T, int D, int ROWS, int NT> struct TileStageT {
+    static constexpr int EPV = 16 / sizeof(T);
+    static constexpr int CPR = D / EPV;          // 16-byte column groups
+    static constexpr int NQ = ROWS / 4;          // row quads
+    static constexpr int UNITS = NQ * CPR;
+    static constexpr int N = (UNITS + NT - 1) / NT;
+    static constexpr int PADT = 16 / sizeof(T);  // 16 bytes of padding per LDS row
+    static constexpr int LDT = ROWS + PADT;
+    static_assert(ROWS % 16 == 0, "row count must be a multiple of 16");
+    static_assert(CPR % 4 == 0, "column groups must come in fours");
+    int4 r[N][4];
+
+    // unit -> (row quad m, column group cg)
+    static __device__ __forceinline__ void unit(int u, int &m, int &cg) {
+        m = (u / 4) % NQ;
+        cg = (u / (4 * NQ)) * 4 + u % 4;
+    }
+
+    __device__ __forceinline__ void load(const T *__restrict__ g, int64_t row0, int nrows, int heads, int h,
+                                         int tid) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + i * NT;
+            int m, cg;
+            unit(u, m, cg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = 4 * m + j;
+                r[i][j] = (u < UNITS && row < nrows)
+                              ? *reinterpret_cast<const int4 *>(g + ((row0 + row) * heads + h) * D + cg * EPV)
+                              : int4{0, 0, 0, 0};
+            }
+        }
+    }
+    // Row-major copy of the same rows (the layout of RowLayout).
+    __device__ __forceinline__ void store_rows(T *lds, int tid) const {
+        using RL = RowLayout<T, D>;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + i * NT;
+            if (UNITS % NT != 0 && u >= UNITS) continue;
+            int m, cg;
+            unit(u, m, cg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) *reinterpret_cast<int4 *>(lds + (4 * m + j) * RL::LD + cg * EPV) = r[i][j];
+        }
+    }
+    __device__ __forceinline__ void store(T *ldsT, int tid) const {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int u = tid + i * NT;
+            if (UNITS % NT != 0 && u >= UNITS) continue;
+            int m, cg;
+            unit(u, m, cg);
+            const int pos = tperm(4 * m);
+            if constexpr (sizeof(T) == 2) {
+                const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&r[i][0]);
+                const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&r[i][1]);
+                const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&r[i][2]);
+                const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&r[i][3]);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    uint2 lo, hi;   // column 2d (low halves) and 2d+1 (high halves), rows 4m..4m+3
+                    lo.x = (w0[d] & 0xffffu) | (w1[d] << 16);
+                    lo.y = (w2[d] & 0xffffu) | (w3[d] << 16);
+                    hi.x = (w0[d] >> 16) | (w1[d] & 0xffff0000u);
+                    hi.y = (w2[d] >> 16) | (w3[d] & 0xffff0000u);
+                    *reinterpret_cast<uint2 *>(ldsT + (cg * EPV + 2 * d) * LDT + pos) = lo;
+                    *reinterpret_cast<uint2 *>(ldsT + (cg * EPV + 2 * d + 1) * LDT + pos) = hi;
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    int4 col;
+                    col.x = reinterpret_cast<const int *>(&r[i][0])[d];
+                    col.y = reinterpret_cast<const int *>(&r[i][1])[d];
+                    col.z = reinterpret_cast<const int *>(&r[i][2])[d];
+                    col.w = reinterpret_cast<const int *>(&r[i][3])[d];
+                    *reinterpret_cast<int4 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
+                }
+            }
         }
     }
 };

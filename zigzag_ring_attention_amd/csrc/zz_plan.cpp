@@ -200,7 +200,9 @@ zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, in
     PassTables &dq = p->pass[ZZ_PASS_BWD_DQ];
     dq.bm = 128; dq.bn = 64; dq.key_major = false; dq.keep_empty = false;
     PassTables &dkv = p->pass[ZZ_PASS_BWD_DKV];
-    dkv.bm = 64; dkv.bn = 128; dkv.key_major = true; dkv.keep_empty = false;
+    // fp32 x 128 query tiles are halved so the double-buffered LDS stage fits.
+    dkv.bm = (dt == ZZ_F32 && d == 128) ? 32 : 64;
+    dkv.bn = 128; dkv.key_major = true; dkv.keep_empty = false;
     for (auto &t : p->pass) build_pass(p, t);
 
     // Workspace image: zigzag map, then items / tiles / order of each pass.
