@@ -220,6 +220,12 @@ def main():
     }
     dom = max(ks, key=lambda n: ks[n]["total_ms"])
     achieved = per_launch[dom] / (ks[dom]["mean_ms"] * 1e-3) / 1e12
+    # HBM bytes per launch of the dominant kernel from the committed counter
+    # summary of this workload (None once the kernel sources have changed).
+    traffic = None
+    if w.name == "c5":
+        from zigzag_ring_attention_amd import profiling
+        traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", "c5_hbm_traffic.txt"), dom + "_kernel")
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     fwd_ms = ks["fwd_step"]["total_ms"] / args.steps
     bwd_ms = (ks["bwd_dkv"]["total_ms"] + ks["bwd_dq"]["total_ms"]) / args.steps if w.backward else 0.0
@@ -286,7 +292,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": traffic,
         },
         "balance": balance,
         "cpu_baseline": cpu,

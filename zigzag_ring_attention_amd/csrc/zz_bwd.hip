@@ -6,21 +6,20 @@
 // summed over the query heads of each key/value group.
 //
 // Two kernels per step, neither uses atomics:
-//  * dkv (key-major): a workgroup owns up to 128 keys of shard j (4 waves x 32
-//    keys) and one key/value head.  It walks every query head of the group and
-//    every listed query tile (up to 64 rows, staged in LDS with its LSE and
-//    delta), forming S and dP with the keys in the lane dimension, so that P
-//    and dS are directly the operands of dV^T += dO^T P and dK^T += Q^T dS.
+//  * dkv (key-major): a workgroup owns up to 128 keys of shard j and one
+//    key/value head.  It walks every query head of the group and every listed
+//    query tile (up to 64 rows, staged in LDS with its LSE and delta), forming
+//    S and dP with the keys in the lane dimension, so that P and dS are
+//    directly the operands of dV^T += dO^T P and dK^T += Q^T dS.
 //  * dq (query-major): like the forward step, S^T and dP^T with the queries in
 //    the lane dimension, then dQ^T += K^T dS^T.
 // Fully masked tiles are never visited (tile lists from the planner).
 
+#include <type_traits>
+
 #include "zz_mfma.h"
 
 // Waves per SIMD each kernel is compiled for (register budget 512 / waves).
-#ifndef ZZ_DKV_WAVES
-#define ZZ_DKV_WAVES 1
-#endif
 #ifndef ZZ_DQ_WAVES
 #define ZZ_DQ_WAVES 2
 #endif
@@ -42,6 +41,7 @@ struct BwdArgs {
     int32_t n, hq, hkv;
     float scale, scale_log2;
     int32_t accumulate;
+    int32_t nitems;   // work items in this launch
 };
 
 // Read-add-write of a lane's column of a transposed accumulator (C layout:
@@ -65,69 +65,79 @@ __device__ __forceinline__ void add_row(float *row, const f32x16 (&acc)[NB], flo
 // ---------------------------------------------------------------- dK, dV
 
 // Query rows per streamed tile (must match the planner's dK/dV tile).
-template <typename T, int D> constexpr int q_tile() { return (sizeof(T) == 4 && D == 128) ? 32 : 64; }
+template <typename T, int D> constexpr int q_tile() { return (sizeof(T) == 4 && D >= 64) ? 32 : 64; }
 
+constexpr int kDkvThreads = 512;
+
+// Eight waves own 128 keys as four pairs of 32 keys.  In a pair, wave A
+// (waves 0-3) forms S = Q K^T and P = exp(S - LSE), hands P to its partner
+// through LDS and accumulates dV^T += dO^T P; wave B (waves 4-7) forms
+// dP = dO V^T, takes P, forms dS = P (dP - delta) and accumulates
+// dK^T += Q^T dS.  Each wave keeps one key-side operand and one accumulator
+// (half of what one wave doing everything would hold), so two waves fit per
+// SIMD, and the two roles of a pair share a SIMD and overlap their matrix
+// and vector work.  Q and dO tiles are staged twice (row-major for S and dP,
+// transposed for dK^T and dV^T) and double-buffered with register prefetch.
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_DKV_WAVES)))
+__global__ void __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkv_kernel(BwdArgs a) {
     constexpr int kQT = q_tile<T, D>();
+    constexpr int NQB = kQT / 32;
     using M = Mfma<T, D>;
-    using TStage = TileStageT<T, D, kQT, kThreads>;
+    using TStage = TileStageT<T, D, kQT, kDkvThreads, 2>;
     constexpr int LD = M::LD;
     constexpr int LDT = TStage::LDT;
     constexpr int NB = D / 32;
-    // Q and dO of the current (head, query tile), each twice: row-major for
-    // S = Q K^T and dP = dO V^T (A operands with the head dim contiguous), and
-    // transposed for dK^T += Q^T dS and dV^T += dO^T P (A operands with the
-    // queries contiguous), so every operand read is a 16-byte LDS read.
-    // Double-buffered: the next tile is loaded into registers during the
-    // current compute and stored to the other buffer; one barrier per tile.
-    // The key-side operands and the dK/dV accumulators stay in registers for
-    // the whole item, which costs the second wave per SIMD.
     __shared__ __attribute__((aligned(16))) T Qs[2][kQT * LD];
     __shared__ __attribute__((aligned(16))) T Ds[2][kQT * LD];
     __shared__ __attribute__((aligned(16))) T QsT[2][D * LDT];
     __shared__ __attribute__((aligned(16))) T DsT[2][D * LDT];
     __shared__ float lse_s[2][kQT], dlt_s[2][kQT];
+    // P handed from wave A to wave B: fp16 for 16-bit inputs (10-bit mantissa,
+    // so the dS that forms dK is close to the one the dQ kernel forms from
+    // the same scores), fp32 otherwise.
+    using PexT = typename std::conditional<sizeof(T) == 2, _Float16, float>::type;
+    __shared__ __attribute__((aligned(16))) PexT Pex[4][NQB][16][64];   // [pair][q block][register][lane]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
-    const int kvh = blockIdx.y;
+    const int pair = wave & 3;
+    const bool role_a = wave < 4;
+    int item_ix, kvh;
+    block_to_work(blockIdx.x, a.nitems, a.hkv, 1, item_ix, kvh);
     const int G = a.hq / a.hkv;
-    const WorkItem it = a.items[a.order ? a.order[blockIdx.x] : blockIdx.x];
+    const WorkItem it = a.items[a.order ? a.order[item_ix] : item_ix];
     const int nkey = it.a1 - it.a0;
-    const int kk = wave * 32 + (lane & 31);          // key offset in the item
+    const int kk = pair * 32 + (lane & 31);          // key offset in the item
     const bool key_ok = kk < nkey;
-    const bool wave_on = wave * 32 < nkey;
+    const bool pair_on = pair * 32 < nkey;           // wave-uniform
     const int64_t krow = (int64_t)it.shard * a.n + it.a0 + kk;   // zigzag row of this lane's key
     const int64_t qrow0 = (int64_t)it.rank * a.n;
     const T *q = static_cast<const T *>(a.q);
     const T *dout = static_cast<const T *>(a.dout);
 
-    typename M::Op kop[M::KS], vop[M::KS];
-    if (key_ok) {
-        M::load_row_op(kop, static_cast<const T *>(a.k) + (krow * a.hkv + kvh) * D, hh);
-        M::load_row_op(vop, static_cast<const T *>(a.v) + (krow * a.hkv + kvh) * D, hh);
-    } else {
-        M::zero_op(kop);
-        M::zero_op(vop);
-    }
-    f32x16 dk[NB], dv[NB];
+    // Key-side operand: K rows for wave A (S), V rows for wave B (dP).
+    typename M::Op op[M::KS];
+    if (key_ok) M::load_row_op(op, static_cast<const T *>(role_a ? a.k : a.v) + (krow * a.hkv + kvh) * D, hh);
+    else M::zero_op(op);
+    f32x16 acc[NB];   // dV^T (wave A) or dK^T (wave B)
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dk[b][i] = dv[b][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
 
     // Walk (query head of the group) x (listed query tile) as one sequence.
     const int ntile = it.tend - it.tbeg;
     const int nwork = G * ntile;
     TStage qt, dt;   // one load each feeds both the row-major and the transposed copy
+    qt.init(a.hq, tid);
+    dt.init(a.hq, tid);
     float lse_r = 0.0f, dlt_r = 0.0f;
     auto fetch = [&](int u) {
         const int h = kvh * G + u / ntile;
         const TileRec tn = a.tiles[it.tbeg + u % ntile];
         const int nq = tn.b1 - tn.b0;
-        qt.load(q, qrow0 + tn.b0, nq, a.hq, h, tid);
-        dt.load(dout, qrow0 + tn.b0, nq, a.hq, h, tid);
+        qt.load(tile_base<T, D>(q, qrow0 + tn.b0, a.hq, h), nq, tid);
+        dt.load(tile_base<T, D>(dout, qrow0 + tn.b0, a.hq, h), nq, tid);
         if (tid < kQT) {
             const bool ok = tid < nq;
             lse_r = ok ? a.lse[(int64_t)h * a.T + qrow0 + tn.b0 + tid] * kLog2e : 0.0f;
@@ -153,35 +163,55 @@ bwd_dkv_kernel(BwdArgs a) {
         const int nq = tr.b1 - tr.b0;
         const bool more = u + 1 < nwork;
         if (more) fetch(u + 1);
-        if (wave_on) {
-            const T *qs = Qs[buf], *ds = Ds[buf], *qst = QsT[buf], *dst = DsT[buf];
-            const float *ls = lse_s[buf], *dl = dlt_s[buf];
+        f32x16 x[NQB];   // wave A: P; wave B: dP
+        if (pair_on) {
 #pragma unroll
-            for (int qb = 0; qb < kQT / 32; ++qb) {
-                if (qb * 32 >= nq) break;
-                f32x16 s, dp;
+            for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
-                M::gemm_rows_lds(s, qs, qb * 32 + (lane & 31), kop, hh);
-                M::gemm_rows_lds(dp, ds, qb * 32 + (lane & 31), vop, hh);
+                for (int i = 0; i < 16; ++i) x[qb][i] = 0.0f;
+                if (qb * 32 < nq)
+                    M::gemm_rows_lds(x[qb], role_a ? Qs[buf] : Ds[buf], qb * 32 + (lane & 31), op, hh);
+            }
+            if (role_a) {
+                const float *ls = lse_s[buf];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int qq = qb * 32 + c_row(i, hh);
-                    const bool vis = qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk);
-                    const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -ls[qq])) : 0.0f;
-                    s[i] = p;
-                    dp[i] = p * (dp[i] - dl[qq]);
+                for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int qq = qb * 32 + c_row(i, hh);
+                        const bool vis = qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk);
+                        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(x[qb][i], a.scale_log2, -ls[qq])) : 0.0f;
+                        x[qb][i] = p;
+                        Pex[pair][qb][i][lane] = static_cast<PexT>(p);
+                    }
+            }
+        }
+        __syncthreads();   // P of every pair is in LDS
+        if (pair_on) {
+            if (role_a) {
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb)
+                    if (qb * 32 < nq) M::template gemm_t_c<LDT>(acc, DsT[buf], qb * 32, x[qb], lane);
+            } else {
+                const float *dl = dlt_s[buf];
+#pragma unroll
+                for (int qb = 0; qb < NQB; ++qb) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int qq = qb * 32 + c_row(i, hh);
+                        const float p = static_cast<float>(Pex[pair][qb][i][lane]);
+                        x[qb][i] = p * (x[qb][i] - dl[qq]);
+                    }
+                    if (qb * 32 < nq) M::template gemm_t_c<LDT>(acc, QsT[buf], qb * 32, x[qb], lane);
                 }
-                M::template gemm_t_c<LDT>(dv, dst, qb * 32, s, lane);
-                M::template gemm_t_c<LDT>(dk, qst, qb * 32, dp, lane);
             }
         }
         if (more) stash(buf ^ 1);
         __syncthreads();
     }
     if (!key_ok) return;
-    add_row<NB>(a.dk + (krow * a.hkv + kvh) * D, dk, a.scale, hh, a.accumulate != 0);
-    add_row<NB>(a.dv + (krow * a.hkv + kvh) * D, dv, 1.0f, hh, a.accumulate != 0);
+    if (role_a) add_row<NB>(a.dv + (krow * a.hkv + kvh) * D, acc, 1.0f, hh, a.accumulate != 0);
+    else add_row<NB>(a.dk + (krow * a.hkv + kvh) * D, acc, a.scale, hh, a.accumulate != 0);
 }
 
 // ---------------------------------------------------------------- dQ
@@ -204,9 +234,10 @@ bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) T Vs[kKT * LD];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
-    const int head = blockIdx.y;
+    int item_ix, head;
+    block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
     const int kvh = head / (a.hq / a.hkv);
-    const WorkItem it = a.items[a.order ? a.order[blockIdx.x] : blockIdx.x];
+    const WorkItem it = a.items[a.order ? a.order[item_ix] : item_ix];
     const int nq = it.a1 - it.a0;
     const int qq = wave * 32 + (lane & 31);
     const bool row_ok = qq < nq;
@@ -235,10 +266,12 @@ bwd_dq_kernel(BwdArgs a) {
 
     RStage vst;
     TStage ktst;   // one load of K feeds both its row-major and transposed copies
+    ktst.init(a.hkv, tid);
+    vst.init(a.hkv, tid);
     {
         const TileRec tr0 = a.tiles[it.tbeg];
-        ktst.load(k, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
-        vst.load(v, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
+        ktst.load(tile_base<T, D>(k, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
+        vst.load(tile_base<T, D>(v, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
     }
     for (int t = it.tbeg; t < it.tend; ++t) {
         const TileRec tr = a.tiles[t];
@@ -250,8 +283,8 @@ bwd_dq_kernel(BwdArgs a) {
         __syncthreads();
         if (t + 1 < it.tend) {       // next tile's loads fly during this compute
             const TileRec tn = a.tiles[t + 1];
-            ktst.load(k, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
-            vst.load(v, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
+            ktst.load(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
+            vst.load(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
         }
         if (!wave_on) continue;
 #pragma unroll
@@ -280,15 +313,15 @@ template <typename T, int D>
 hipError_t launch_t(const zz_plan *p, int rank, int step, BwdArgs a, int which, hipStream_t st) {
     const Launch Lkv = launch_items(p, ZZ_PASS_BWD_DKV, rank, step);
     if ((which & 1) && Lkv.n > 0) {
-        a.items = Lkv.items; a.order = Lkv.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DKV);
-        hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), dim3(Lkv.n, p->hkv), dim3(kThreads), 0, st, a);
+        a.items = Lkv.items; a.order = Lkv.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DKV); a.nitems = Lkv.n;
+        hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), dim3(Lkv.n * p->hkv), dim3(kDkvThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const Launch Lq = launch_items(p, ZZ_PASS_BWD_DQ, rank, step);
     if ((which & 2) && Lq.n > 0) {
-        a.items = Lq.items; a.order = Lq.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DQ);
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(Lq.n, p->hq), dim3(kThreads), 0, st, a);
+        a.items = Lq.items; a.order = Lq.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DQ); a.nitems = Lq.n;
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(Lq.n * p->hq), dim3(kThreads), 0, st, a);
     }
     return hipGetLastError();
 }

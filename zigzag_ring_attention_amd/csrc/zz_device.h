@@ -42,6 +42,27 @@ __device__ __forceinline__ float merge_value(const MergeWeights &w, float oa, fl
     return fmaf(w.wa, oa, w.wb * ob);
 }
 
+// Map a 1-D workgroup index to (work item, head).  Workgroups are dealt to
+// the 8 XCDs of the chip round-robin, and each XCD has its own L2; when the
+// key/value heads split evenly over the XCDs, every XCD gets whole key/value
+// groups, and consecutive workgroups on an XCD are the G query heads of one
+// item, so the workgroups that read the same K/V tiles share an L2.
+// `group` = query heads per key/value head (1 for the key-major pass).
+__device__ __forceinline__ void block_to_work(int b, int nitems, int nheads, int group, int &item, int &head) {
+    const int nkv = nheads / group;
+    if (nkv % 8 == 0) {
+        const int x = b % 8, t = b / 8;
+        const int per = nitems * group;
+        const int kvh = x + 8 * (t / per);
+        const int rem = t - (t / per) * per;
+        item = rem / group;
+        head = kvh * group + rem % group;
+    } else {
+        item = b / nheads;
+        head = b % nheads;
+    }
+}
+
 // float -> bf16, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
 

@@ -43,6 +43,7 @@ struct FwdArgs {
     int32_t hq, hkv;
     float scale_log2;   // softmax scale * log2(e)
     int32_t merge;
+    int32_t nitems;     // work items in this launch
 };
 
 template <typename T, int D>
@@ -59,9 +60,10 @@ fwd_step_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) T Vt[2][D * LDT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
-    const int head = blockIdx.y;
+    int item_ix, head;
+    block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
     const int kvh = head / (a.hq / a.hkv);
-    const WorkItem it = a.items[a.order ? a.order[blockIdx.x] : blockIdx.x];
+    const WorkItem it = a.items[a.order ? a.order[item_ix] : item_ix];
     const int nq = it.a1 - it.a0;
     const int qq = wave * 32 + (lane & 31);          // query offset in the item
     const bool row_ok = qq < nq;
@@ -100,10 +102,12 @@ fwd_step_kernel(FwdArgs a) {
 
     TileStage<T, D, kBN, kThreads> kst;
     VStage vst;
+    kst.init(a.hkv, tid);
+    vst.init(a.hkv, tid);
     {
         const TileRec tr0 = a.tiles[it.tbeg];
-        kst.load(k, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
-        vst.load(v, kv_row0 + tr0.b0, tr0.b1 - tr0.b0, a.hkv, kvh, tid);
+        kst.load(tile_base<T, D>(k, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
+        vst.load(tile_base<T, D>(v, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
         kst.store(Ks[0], tid);
         vst.store(Vt[0], tid);
     }
@@ -115,8 +119,8 @@ fwd_step_kernel(FwdArgs a) {
         const bool more = t + 1 < it.tend;
         if (more) {                  // next tile's loads fly while this one is computed
             const TileRec tn = a.tiles[t + 1];
-            kst.load(k, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
-            vst.load(v, kv_row0 + tn.b0, tn.b1 - tn.b0, a.hkv, kvh, tid);
+            kst.load(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
+            vst.load(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
         }
         if (wave_on) {
             const T *ks = Ks[buf];
@@ -224,7 +228,8 @@ hipError_t launch_t(const zz_plan *p, const Launch &L, const void *q, const void
     a.T = p->T; a.n = (int32_t)(p->T / p->cp); a.hq = p->hq; a.hkv = p->hkv;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
     a.merge = merge;
-    hipLaunchKernelGGL((fwd_step_kernel<T, D>), dim3(L.n, p->hq), dim3(kThreads), 0, st, a);
+    a.nitems = L.n;
+    hipLaunchKernelGGL((fwd_step_kernel<T, D>), dim3(L.n * p->hq), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -131,6 +131,14 @@ template <int D> struct Mfma<float, D> {
     }
 };
 
+// Address of row `row0` of head h in a [*, heads, D] tensor: the tile base
+// every thread adds its own loop-invariant byte offset to (the base is
+// wave-uniform, so loads take the scalar-base + 32-bit-offset form).
+template <typename T, int D>
+__device__ __forceinline__ const char *tile_base(const T *g, int64_t row0, int heads, int h) {
+    return reinterpret_cast<const char *>(g + (row0 * heads + h) * D);
+}
+
 // A tile of ROWS rows x D columns of a [*, H, D] tensor (one head), staged
 // global -> registers -> LDS by NT threads.  Issuing the global loads for the
 // next tile before computing on the current one hides their latency.
@@ -142,15 +150,25 @@ template <typename T, int D, int ROWS, int NT> struct TileStage {
     static_assert(N >= 1 && (ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
     static constexpr int LD = RowLayout<T, D>::LD;
     int4 r[N];
+    uint32_t voff[N];   // byte offset of this thread's chunks from the tile base
 
-
-    __device__ __forceinline__ void load(const T *__restrict__ g, int64_t row0, int nrows, int heads, int h,
-                                         int tid) {
+    __device__ __forceinline__ void init(int heads, int tid) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
             const int c = tid + i * NT, row = c / CPR, e = (c % CPR) * EPV;
-            r[i] = row < nrows ? *reinterpret_cast<const int4 *>(g + ((row0 + row) * heads + h) * D + e)
-                               : int4{0, 0, 0, 0};
+            voff[i] = (uint32_t)((row * heads * D + e) * sizeof(T));
+        }
+    }
+    __device__ __forceinline__ void load(const char *base, int nrows, int tid) {
+        if (nrows == ROWS) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) r[i] = *reinterpret_cast<const int4 *>(base + voff[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int row = (tid + i * NT) / CPR;
+                r[i] = row < nrows ? *reinterpret_cast<const int4 *>(base + voff[i]) : int4{0, 0, 0, 0};
+            }
         }
     }
     __device__ __forceinline__ void store(T *lds, int tid) const {
@@ -164,43 +182,58 @@ template <typename T, int D, int ROWS, int NT> struct TileStage {
 
 // A tile of ROWS rows x D columns of a [*, H, D] tensor (one head), staged
 // into LDS transposed: LDS row c holds column c of the tile, the tile rows
-// placed at tperm(row).  Each thread gathers 4 rows x one 16-byte column
-// group, regroups them in registers, and writes 4 consecutive rows per LDS
-// column (8 bytes for bf16, 16 for fp32).  The same registers also give the
-// row-major copy (store_rows).  Lanes are laid out as 4 column groups x 16
-// row quads x the rest of the column groups: the row-major stores of 16
-// lanes then cover 16 distinct bank groups of the padded layout.
-template <typename T, int D, int ROWS, int NT> struct TileStageT {
+// placed at tperm(row).  Each thread gathers RPU (4 or 2) consecutive rows x
+// one 16-byte column group, regroups them in registers, and writes RPU
+// consecutive rows per LDS column.  The same registers also give the
+// row-major copy (store_rows).  Lanes are laid out as 4 column groups x the
+// row units x the rest of the column groups, which keeps the stores of 16
+// lanes on distinct (RPU 4) or at most two-way shared (RPU 2) bank groups.
+template <typename T, int D, int ROWS, int NT, int RPU = 4> struct TileStageT {
     static constexpr int EPV = 16 / sizeof(T);
     static constexpr int CPR = D / EPV;          // 16-byte column groups
-    static constexpr int NQ = ROWS / 4;          // row quads
+    static constexpr int NQ = ROWS / RPU;        // row units
     static constexpr int UNITS = NQ * CPR;
     static constexpr int N = (UNITS + NT - 1) / NT;
     static constexpr int PADT = 16 / sizeof(T);  // 16 bytes of padding per LDS row
     static constexpr int LDT = ROWS + PADT;
     static_assert(ROWS % 16 == 0, "row count must be a multiple of 16");
     static_assert(CPR % 4 == 0, "column groups must come in fours");
-    int4 r[N][4];
+    static_assert(RPU == 4 || RPU == 2, "2 or 4 rows per unit");
+    int4 r[N][RPU];
+    uint32_t voff[N];   // byte offset of row RPU*m, column group cg from the tile base
+    uint32_t rstride;   // bytes between consecutive rows (wave-uniform)
 
-    // unit -> (row quad m, column group cg)
+    // unit -> (row unit m, column group cg)
     static __device__ __forceinline__ void unit(int u, int &m, int &cg) {
         m = (u / 4) % NQ;
         cg = (u / (4 * NQ)) * 4 + u % 4;
     }
-
-    __device__ __forceinline__ void load(const T *__restrict__ g, int64_t row0, int nrows, int heads, int h,
-                                         int tid) {
+    __device__ __forceinline__ void init(int heads, int tid) {
+        rstride = (uint32_t)(heads * D * sizeof(T));
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int u = tid + i * NT;
             int m, cg;
-            unit(u, m, cg);
+            unit(tid + i * NT, m, cg);
+            voff[i] = (uint32_t)(RPU * m) * rstride + (uint32_t)(cg * EPV * sizeof(T));
+        }
+    }
+    __device__ __forceinline__ void load(const char *base, int nrows, int tid) {
+        if (nrows == ROWS && UNITS % NT == 0) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int row = 4 * m + j;
-                r[i][j] = (u < UNITS && row < nrows)
-                              ? *reinterpret_cast<const int4 *>(g + ((row0 + row) * heads + h) * D + cg * EPV)
-                              : int4{0, 0, 0, 0};
+            for (int i = 0; i < N; ++i)
+#pragma unroll
+                for (int j = 0; j < RPU; ++j) r[i][j] = *reinterpret_cast<const int4 *>(base + j * rstride + voff[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int u = tid + i * NT;
+                int m, cg;
+                unit(u, m, cg);
+#pragma unroll
+                for (int j = 0; j < RPU; ++j)
+                    r[i][j] = (u < UNITS && RPU * m + j < nrows)
+                                  ? *reinterpret_cast<const int4 *>(base + j * rstride + voff[i])
+                                  : int4{0, 0, 0, 0};
             }
         }
     }
@@ -214,7 +247,7 @@ template <typename T, int D, int ROWS, int NT> struct TileStageT {
             int m, cg;
             unit(u, m, cg);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) *reinterpret_cast<int4 *>(lds + (4 * m + j) * RL::LD + cg * EPV) = r[i][j];
+            for (int j = 0; j < RPU; ++j) *reinterpret_cast<int4 *>(lds + (RPU * m + j) * RL::LD + cg * EPV) = r[i][j];
         }
     }
     __device__ __forceinline__ void store(T *ldsT, int tid) const {
@@ -224,10 +257,10 @@ template <typename T, int D, int ROWS, int NT> struct TileStageT {
             if (UNITS % NT != 0 && u >= UNITS) continue;
             int m, cg;
             unit(u, m, cg);
-            const int pos = tperm(4 * m);
-            if constexpr (sizeof(T) == 2) {
-                const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&r[i][0]);
-                const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&r[i][1]);
+            const int pos = tperm(RPU * m);
+            const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&r[i][0]);
+            const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&r[i][1]);
+            if constexpr (sizeof(T) == 2 && RPU == 4) {
                 const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&r[i][2]);
                 const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&r[i][3]);
 #pragma unroll
@@ -240,7 +273,15 @@ template <typename T, int D, int ROWS, int NT> struct TileStageT {
                     *reinterpret_cast<uint2 *>(ldsT + (cg * EPV + 2 * d) * LDT + pos) = lo;
                     *reinterpret_cast<uint2 *>(ldsT + (cg * EPV + 2 * d + 1) * LDT + pos) = hi;
                 }
-            } else {
+            } else if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t lo = (w0[d] & 0xffffu) | (w1[d] << 16);
+                    const uint32_t hi = (w0[d] >> 16) | (w1[d] & 0xffff0000u);
+                    *reinterpret_cast<uint32_t *>(ldsT + (cg * EPV + 2 * d) * LDT + pos) = lo;
+                    *reinterpret_cast<uint32_t *>(ldsT + (cg * EPV + 2 * d + 1) * LDT + pos) = hi;
+                }
+            } else if constexpr (RPU == 4) {
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     int4 col;
@@ -249,6 +290,14 @@ template <typename T, int D, int ROWS, int NT> struct TileStageT {
                     col.z = reinterpret_cast<const int *>(&r[i][2])[d];
                     col.w = reinterpret_cast<const int *>(&r[i][3])[d];
                     *reinterpret_cast<int4 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
+                }
+            } else {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    int2 col;
+                    col.x = reinterpret_cast<const int *>(&r[i][0])[d];
+                    col.y = reinterpret_cast<const int *>(&r[i][1])[d];
+                    *reinterpret_cast<int2 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
                 }
             }
         }

@@ -200,8 +200,9 @@ zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, in
     PassTables &dq = p->pass[ZZ_PASS_BWD_DQ];
     dq.bm = 128; dq.bn = 64; dq.key_major = false; dq.keep_empty = false;
     PassTables &dkv = p->pass[ZZ_PASS_BWD_DKV];
-    // fp32 x 128 query tiles are halved so the double-buffered LDS stage fits.
-    dkv.bm = (dt == ZZ_F32 && d == 128) ? 32 : 64;
+    // fp32 query tiles of 64 or 128 columns are halved so the double-buffered
+    // LDS stage of the dK/dV kernel fits.
+    dkv.bm = (dt == ZZ_F32 && d >= 64) ? 32 : 64;
     dkv.bn = 128; dkv.key_major = true; dkv.keep_empty = false;
     for (auto &t : p->pass) build_pass(p, t);
 

@@ -1,0 +1,117 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+    python -m zigzag_ring_attention_amd.profiling stats  <kernel_stats.csv> <command...>
+    python -m zigzag_ring_attention_amd.profiling traffic <fetch.csv> <write.csv> <command...>
+
+``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown
+table.  ``traffic`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
+counter_collection.csv files into HBM bytes per launch of each libzz kernel.
+The counters are calibrated against the zigzag permute kernel in the same
+run, a plain row copy whose bytes are known exactly: the first permute of a
+bench step moves T * Hq * d * 2 bytes each way.
+
+The traffic summary records a hash of the kernel sources; ``read_traffic``
+returns nothing for a kernel once the sources have changed since the
+counters were taken.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import hashlib
+import os
+import re
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["zz_fwd.hip", "zz_bwd.hip", "zz_mfma.h", "zz_device.h", "zz_util.hip", "zz_internal.h"]
+_NAMES = ["fwd_step_kernel", "bwd_dkv_kernel", "bwd_dq_kernel", "permute_kernel", "cast_rows_kernel",
+          "bwd_pre_kernel", "lse_merge_kernel", "debug_mask_kernel"]
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "csrc", name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    for n in _NAMES:
+        if n in name:
+            return n
+    return name[:48]
+
+
+def stats_markdown(path: str, command: str) -> str:
+    rows = list(csv.DictReader(open(path)))
+    out = ["# Kernel time, rocprofv3 --kernel-trace --stats", "",
+           "Command: `%s`" % command, "",
+           "| kernel | calls | total ms | average ms | min ms | max ms | % |",
+           "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| %s | %s | %.3f | %.4f | %.4f | %.4f | %.2f |" % (
+            short_name(r["Name"]), r["Calls"], float(r["TotalDurationNs"]) / 1e6,
+            float(r["AverageNs"]) / 1e6, float(r["MinNs"]) / 1e6, float(r["MaxNs"]) / 1e6,
+            float(r["Percentage"])))
+    return "\n".join(out) + "\n"
+
+
+def _per_dispatch(path: str, counter: str):
+    vals = collections.defaultdict(list)
+    grid = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        k = short_name(r["Kernel_Name"])
+        vals[k].append(float(r["Counter_Value"]))
+        grid.setdefault(k, []).append(int(r["Grid_Size"]))
+    return vals, grid
+
+
+def traffic_text(fetch_csv: str, write_csv: str, command: str, copy_bytes: float) -> str:
+    f, _ = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    w, _ = _per_dispatch(write_csv, "WRITE_SIZE")
+    # calibration: the first permute of the step copies copy_bytes each way
+    f_cal = copy_bytes / (f["permute_kernel"][0] * 1024.0)
+    w_cal = copy_bytes / (w["permute_kernel"][0] * 1024.0)
+    lines = ["# HBM traffic per launch, rocprofv3 --pmc FETCH_SIZE then --pmc WRITE_SIZE (KiB per dispatch)",
+             "# command: %s" % command,
+             "# calibration: first permute_kernel dispatch copies %d bytes each way;" % int(copy_bytes),
+             "#   bytes = FETCH_SIZE KiB * 1024 * %.4f, WRITE_SIZE KiB * 1024 * %.4f" % (f_cal, w_cal),
+             "kernel_sources_sha256 %s" % sources_hash(),
+             "fetch_calibration %.6f" % f_cal,
+             "write_calibration %.6f" % w_cal]
+    for k in sorted(set(f) & set(w)):
+        fk = sum(f[k]) / len(f[k])
+        wk = sum(w[k]) / len(w[k])
+        lines.append("kernel %s dispatches %d fetch_kib %.1f write_kib %.1f hbm_bytes_per_launch %.6e"
+                     % (k, len(f[k]), fk, wk, fk * 1024 * f_cal + wk * 1024 * w_cal))
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic(path: str, kernel: str):
+    """HBM bytes per launch of `kernel` from a traffic summary, or None if the
+    file is missing or the kernel sources changed since it was taken."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^kernel_sources_sha256 (\S+)", text, re.M)
+    if not m or m.group(1) != sources_hash():
+        return None
+    m = re.search(r"^kernel %s .* hbm_bytes_per_launch (\S+)" % re.escape(kernel), text, re.M)
+    return float(m.group(1)) if m else None
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        sys.stdout.write(stats_markdown(sys.argv[2], " ".join(sys.argv[3:])))
+    elif sys.argv[1] == "traffic":
+        # copy size of the first permute: Q of the 131072-token, 64-head, d=128 bf16 workload
+        import synthetic
+        w = synthetic.WORKLOADS["c5"]
+        copy_bytes = float(w.total * w.hq * w.d * 2)
+        sys.stdout.write(traffic_text(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]), copy_bytes))
+    else:
+        raise SystemExit("usage: profiling.py stats|traffic ...")
