@@ -92,12 +92,15 @@ bwd_dkv_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) T Ds[2][kQT * LD];
     __shared__ __attribute__((aligned(16))) T QsT[2][D * LDT];
     __shared__ __attribute__((aligned(16))) T DsT[2][D * LDT];
-    __shared__ float lse_s[2][kQT], dlt_s[2][kQT];
+    __shared__ __attribute__((aligned(16))) float lse_s[2][kQT], dlt_s[2][kQT];
     // P handed from wave A to wave B: fp16 for 16-bit inputs (10-bit mantissa,
     // so the dS that forms dK is close to the one the dQ kernel forms from
     // the same scores), fp32 otherwise.
+    // Stored as 16-byte vectors [pair][q block][vector][lane] so a lane moves
+    // its 16 values with 2 (fp16) or 4 (fp32) wide LDS accesses.
     using PexT = typename std::conditional<sizeof(T) == 2, _Float16, float>::type;
-    __shared__ __attribute__((aligned(16))) PexT Pex[4][NQB][16][64];   // [pair][q block][register][lane]
+    constexpr int PPV = 16 / sizeof(PexT);     // values per 16-byte vector
+    __shared__ __attribute__((aligned(16))) uint4 Pex[4][NQB][16 / PPV][64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
     const int pair = wave & 3;
@@ -174,16 +177,33 @@ bwd_dkv_kernel(BwdArgs a) {
             }
             if (role_a) {
                 const float *ls = lse_s[buf];
+                // Full tiles of a full item need no mask (the common case).
+                const bool full = tr.kind == ZZ_TILE_FULL && nq == kQT && nkey == 4 * 32;
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb)
+                for (int qb = 0; qb < NQB; ++qb) {
+                    float4 l4[4];   // LSE of this lane's 16 query rows (4 runs of 4)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4)
+                        l4[i4] = *reinterpret_cast<const float4 *>(ls + qb * 32 + c_row(4 * i4, hh));
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int qq = qb * 32 + c_row(i, hh);
-                        const bool vis = qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk);
-                        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(x[qb][i], a.scale_log2, -ls[qq])) : 0.0f;
+                        const float lv = i % 4 == 0 ? l4[i / 4].x : i % 4 == 1 ? l4[i / 4].y
+                                       : i % 4 == 2 ? l4[i / 4].z : l4[i / 4].w;
+                        float p = __builtin_amdgcn_exp2f(fmaf(x[qb][i], a.scale_log2, -lv));
+                        if (!full) {
+                            const int qq = qb * 32 + c_row(i, hh);
+                            if (!(qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk))) p = 0.0f;
+                        }
                         x[qb][i] = p;
-                        Pex[pair][qb][i][lane] = static_cast<PexT>(p);
                     }
+#pragma unroll
+                    for (int vi = 0; vi < 16 / PPV; ++vi) {
+                        PexT pv[PPV];
+#pragma unroll
+                        for (int e = 0; e < PPV; ++e) pv[e] = static_cast<PexT>(x[qb][vi * PPV + e]);
+                        Pex[pair][qb][vi][lane] = *reinterpret_cast<const uint4 *>(pv);
+                    }
+                }
             }
         }
         __syncthreads();   // P of every pair is in LDS
@@ -196,11 +216,21 @@ bwd_dkv_kernel(BwdArgs a) {
                 const float *dl = dlt_s[buf];
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
+                    float4 d4[4];
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int qq = qb * 32 + c_row(i, hh);
-                        const float p = static_cast<float>(Pex[pair][qb][i][lane]);
-                        x[qb][i] = p * (x[qb][i] - dl[qq]);
+                    for (int i4 = 0; i4 < 4; ++i4)
+                        d4[i4] = *reinterpret_cast<const float4 *>(dl + qb * 32 + c_row(4 * i4, hh));
+#pragma unroll
+                    for (int vi = 0; vi < 16 / PPV; ++vi) {
+                        const uint4 raw = Pex[pair][qb][vi][lane];
+                        const PexT *pv = reinterpret_cast<const PexT *>(&raw);
+#pragma unroll
+                        for (int e = 0; e < PPV; ++e) {
+                            const int i = vi * PPV + e;
+                            const float dv = i % 4 == 0 ? d4[i / 4].x : i % 4 == 1 ? d4[i / 4].y
+                                           : i % 4 == 2 ? d4[i / 4].z : d4[i / 4].w;
+                            x[qb][i] = static_cast<float>(pv[e]) * (x[qb][i] - dv);
+                        }
                     }
                     if (qb * 32 < nq) M::template gemm_t_c<LDT>(acc, QsT[buf], qb * 32, x[qb], lane);
                 }
@@ -295,11 +325,14 @@ bwd_dq_kernel(BwdArgs a) {
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
             M::gemm_rows_lds(s, Ks, kb * 32 + (lane & 31), qop, hh);
             M::gemm_rows_lds(dp, Vs, kb * 32 + (lane & 31), dop, hh);
+            const bool full = tr.kind == ZZ_TILE_FULL && nk == kKT && nq == 4 * 32;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int kk = kb * 32 + c_row(i, hh);
-                const bool vis = kk < nk && row_ok && tile_visible(tr.kind, tr.delta, qq, kk);
-                const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2)) : 0.0f;
+                float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
+                if (!full) {
+                    const int kk = kb * 32 + c_row(i, hh);
+                    if (!(kk < nk && row_ok && tile_visible(tr.kind, tr.delta, qq, kk))) p = 0.0f;
+                }
                 dp[i] = p * (dp[i] - dlt);
             }
             M::template gemm_t_c<LDT>(acc, KsT, kb * 32, dp, lane);
