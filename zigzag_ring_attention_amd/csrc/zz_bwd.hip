@@ -108,7 +108,7 @@ bwd_dkv_kernel(BwdArgs a) {
     int item_ix, kvh;
     block_to_work(blockIdx.x, a.nitems, a.hkv, 1, item_ix, kvh);
     const int G = a.hq / a.hkv;
-    const WorkItem it = a.items[a.order ? a.order[item_ix] : item_ix];
+    const WorkItem it = load_const(a.items, a.order ? load_const(a.order, item_ix) : item_ix);
     const int nkey = it.a1 - it.a0;
     const int kk = pair * 32 + (lane & 31);          // key offset in the item
     const bool key_ok = kk < nkey;
@@ -137,13 +137,14 @@ bwd_dkv_kernel(BwdArgs a) {
     float lse_r = 0.0f, dlt_r = 0.0f;
     auto fetch = [&](int u) {
         const int h = kvh * G + u / ntile;
-        const TileRec tn = a.tiles[it.tbeg + u % ntile];
+        const TileRec tn = load_const(a.tiles, it.tbeg + u % ntile);
         const int nq = tn.b1 - tn.b0;
         qt.load(tile_base<T, D>(q, qrow0 + tn.b0, a.hq, h), nq, tid);
         dt.load(tile_base<T, D>(dout, qrow0 + tn.b0, a.hq, h), nq, tid);
         if (tid < kQT) {
             const bool ok = tid < nq;
-            lse_r = ok ? a.lse[(int64_t)h * a.T + qrow0 + tn.b0 + tid] * kLog2e : 0.0f;
+            // rows past the tile get LSE = +inf, so their P (and dS) is exactly 0
+            lse_r = ok ? a.lse[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : INFINITY;   // scaled when stashed
             dlt_r = ok ? a.delta[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : 0.0f;
         }
     };
@@ -153,7 +154,7 @@ bwd_dkv_kernel(BwdArgs a) {
         qt.store(QsT[buf], tid);
         dt.store(DsT[buf], tid);
         if (tid < kQT) {
-            lse_s[buf][tid] = lse_r;
+            lse_s[buf][tid] = lse_r * kLog2e;
             dlt_s[buf][tid] = dlt_r;
         }
     };
@@ -162,8 +163,7 @@ bwd_dkv_kernel(BwdArgs a) {
     __syncthreads();
     for (int u = 0; u < nwork; ++u) {
         const int buf = u & 1;
-        const TileRec tr = a.tiles[it.tbeg + u % ntile];
-        const int nq = tr.b1 - tr.b0;
+        const TileRec tr = load_const(a.tiles, it.tbeg + u % ntile);
         const bool more = u + 1 < nwork;
         if (more) fetch(u + 1);
         f32x16 x[NQB];   // wave A: P; wave B: dP
@@ -172,13 +172,18 @@ bwd_dkv_kernel(BwdArgs a) {
             for (int qb = 0; qb < NQB; ++qb) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) x[qb][i] = 0.0f;
-                if (qb * 32 < nq)
-                    M::gemm_rows_lds(x[qb], role_a ? Qs[buf] : Ds[buf], qb * 32 + (lane & 31), op, hh);
+                M::gemm_rows_lds(x[qb], role_a ? Qs[buf] : Ds[buf], qb * 32 + (lane & 31), op, hh);
             }
             if (role_a) {
                 const float *ls = lse_s[buf];
-                // Full tiles of a full item need no mask (the common case).
-                const bool full = tr.kind == ZZ_TILE_FULL && nq == kQT && nkey == 4 * 32;
+                // Only partial (diagonal) tiles need a mask: query rows past a
+                // ragged tile have P = 0 through their LSE, and the columns of
+                // keys past a ragged item are never written.  Query row qq
+                // sees key kk iff qq >= kk - delta.
+                if (tr.kind != ZZ_TILE_FULL) {
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) mask_rows_below(x[qb], kk - tr.delta - qb * 32 - 4 * hh);
+                }
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     float4 l4[4];   // LSE of this lane's 16 query rows (4 runs of 4)
@@ -189,12 +194,7 @@ bwd_dkv_kernel(BwdArgs a) {
                     for (int i = 0; i < 16; ++i) {
                         const float lv = i % 4 == 0 ? l4[i / 4].x : i % 4 == 1 ? l4[i / 4].y
                                        : i % 4 == 2 ? l4[i / 4].z : l4[i / 4].w;
-                        float p = __builtin_amdgcn_exp2f(fmaf(x[qb][i], a.scale_log2, -lv));
-                        if (!full) {
-                            const int qq = qb * 32 + c_row(i, hh);
-                            if (!(qq < nq && key_ok && tile_visible(tr.kind, tr.delta, qq, kk))) p = 0.0f;
-                        }
-                        x[qb][i] = p;
+                        x[qb][i] = __builtin_amdgcn_exp2f(fmaf(x[qb][i], a.scale_log2, -lv));
                     }
 #pragma unroll
                     for (int vi = 0; vi < 16 / PPV; ++vi) {
@@ -211,7 +211,7 @@ bwd_dkv_kernel(BwdArgs a) {
             if (role_a) {
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb)
-                    if (qb * 32 < nq) M::template gemm_t_c<LDT>(acc, DsT[buf], qb * 32, x[qb], lane);
+                    M::template gemm_t_c<LDT>(acc, DsT[buf], qb * 32, x[qb], lane);
             } else {
                 const float *dl = dlt_s[buf];
 #pragma unroll
@@ -232,7 +232,7 @@ bwd_dkv_kernel(BwdArgs a) {
                             x[qb][i] = static_cast<float>(pv[e]) * (x[qb][i] - dv);
                         }
                     }
-                    if (qb * 32 < nq) M::template gemm_t_c<LDT>(acc, QsT[buf], qb * 32, x[qb], lane);
+                    M::template gemm_t_c<LDT>(acc, QsT[buf], qb * 32, x[qb], lane);
                 }
             }
         }
@@ -267,7 +267,7 @@ bwd_dq_kernel(BwdArgs a) {
     int item_ix, head;
     block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
     const int kvh = head / (a.hq / a.hkv);
-    const WorkItem it = a.items[a.order ? a.order[item_ix] : item_ix];
+    const WorkItem it = load_const(a.items, a.order ? load_const(a.order, item_ix) : item_ix);
     const int nq = it.a1 - it.a0;
     const int qq = wave * 32 + (lane & 31);
     const bool row_ok = qq < nq;
@@ -299,12 +299,12 @@ bwd_dq_kernel(BwdArgs a) {
     ktst.init(a.hkv, tid);
     vst.init(a.hkv, tid);
     {
-        const TileRec tr0 = a.tiles[it.tbeg];
+        const TileRec tr0 = load_const(a.tiles, it.tbeg);
         ktst.load(tile_base<T, D>(k, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
         vst.load(tile_base<T, D>(v, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
     }
     for (int t = it.tbeg; t < it.tend; ++t) {
-        const TileRec tr = a.tiles[t];
+        const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
         __syncthreads();
         ktst.store_rows(Ks, tid);
@@ -312,27 +312,26 @@ bwd_dq_kernel(BwdArgs a) {
         vst.store(Vs, tid);
         __syncthreads();
         if (t + 1 < it.tend) {       // next tile's loads fly during this compute
-            const TileRec tn = a.tiles[t + 1];
+            const TileRec tn = load_const(a.tiles, t + 1);
             ktst.load(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
             vst.load(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
         }
         if (!wave_on) continue;
 #pragma unroll
         for (int kb = 0; kb < kKT / 32; ++kb) {
-            if (kb * 32 >= nk) break;
             f32x16 s, dp;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
             M::gemm_rows_lds(s, Ks, kb * 32 + (lane & 31), qop, hh);
             M::gemm_rows_lds(dp, Vs, kb * 32 + (lane & 31), dop, hh);
-            const bool full = tr.kind == ZZ_TILE_FULL && nk == kKT && nq == 4 * 32;
+            // mask (partial and ragged tiles only): key kk is kept iff kk < nk
+            // and, in a partial tile, kk <= qq + delta; rows of queries past
+            // the item are never written
+            if (tr.kind != ZZ_TILE_FULL || nk < kKT)
+                mask_rows_above(s, (tr.kind == ZZ_TILE_FULL ? nk - 1 : min(nk - 1, qq + tr.delta)) - kb * 32 - 4 * hh);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
-                if (!full) {
-                    const int kk = kb * 32 + c_row(i, hh);
-                    if (!(kk < nk && row_ok && tile_visible(tr.kind, tr.delta, qq, kk))) p = 0.0f;
-                }
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
                 dp[i] = p * (dp[i] - dlt);
             }
             M::template gemm_t_c<LDT>(acc, KsT, kb * 32, dp, lane);

@@ -63,6 +63,22 @@ __device__ __forceinline__ void block_to_work(int b, int nitems, int nheads, int
     }
 }
 
+// Read of a table that stays constant for the whole launch (work items, tile
+// lists) through the constant address space: with a wave-uniform index the
+// compiler can use a scalar load, whose short latency and separate counter
+// keep it off the path of the vector loads in flight.
+template <typename T>
+__device__ __forceinline__ T load_const(const T *p, int64_t i) {
+    static_assert(sizeof(T) % 4 == 0, "tables hold 32-bit fields");
+    typedef const int32_t __attribute__((address_space(4))) *ConstPtr;
+    const ConstPtr src = (ConstPtr)(p + i);
+    T out;
+    int32_t *dst = reinterpret_cast<int32_t *>(&out);
+#pragma unroll
+    for (unsigned k = 0; k < sizeof(T) / 4; ++k) dst[k] = src[k];
+    return out;
+}
+
 // float -> bf16, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
 

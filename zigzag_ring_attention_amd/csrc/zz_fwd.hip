@@ -63,7 +63,7 @@ fwd_step_kernel(FwdArgs a) {
     int item_ix, head;
     block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
     const int kvh = head / (a.hq / a.hkv);
-    const WorkItem it = a.items[a.order ? a.order[item_ix] : item_ix];
+    const WorkItem it = load_const(a.items, a.order ? load_const(a.order, item_ix) : item_ix);
     const int nq = it.a1 - it.a0;
     const int qq = wave * 32 + (lane & 31);          // query offset in the item
     const bool row_ok = qq < nq;
@@ -105,7 +105,7 @@ fwd_step_kernel(FwdArgs a) {
     kst.init(a.hkv, tid);
     vst.init(a.hkv, tid);
     {
-        const TileRec tr0 = a.tiles[it.tbeg];
+        const TileRec tr0 = load_const(a.tiles, it.tbeg);
         kst.load(tile_base<T, D>(k, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
         vst.load(tile_base<T, D>(v, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
         kst.store(Ks[0], tid);
@@ -114,11 +114,11 @@ fwd_step_kernel(FwdArgs a) {
     __syncthreads();
     for (int t = it.tbeg; t < it.tend; ++t) {
         const int buf = (t - it.tbeg) & 1;
-        const TileRec tr = a.tiles[t];
+        const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
         const bool more = t + 1 < it.tend;
         if (more) {                  // next tile's loads fly while this one is computed
-            const TileRec tn = a.tiles[t + 1];
+            const TileRec tn = load_const(a.tiles, t + 1);
             kst.load(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
             vst.load(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
         }
@@ -130,17 +130,14 @@ fwd_step_kernel(FwdArgs a) {
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-                if (kb == 0 || nk > 32) M::gemm_rows_lds(s[kb], ks, kb * 32 + (lane & 31), qop, hh);
+                M::gemm_rows_lds(s[kb], ks, kb * 32 + (lane & 31), qop, hh);
             }
-            // mask (partial and ragged tiles only), raw block maximum
+            // mask (partial and ragged tiles only): key kk is kept iff
+            // kk < nk and, in a partial tile, kk <= qq + delta
             if (tr.kind != ZZ_TILE_FULL || nk < kBN) {
+                const int last = tr.kind == ZZ_TILE_FULL ? nk - 1 : min(nk - 1, qq + tr.delta);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int kk = kb * 32 + c_row(i, hh);
-                        if (kk >= nk || !tile_visible(tr.kind, tr.delta, qq, kk)) s[kb][i] = -INFINITY;
-                    }
+                for (int kb = 0; kb < 2; ++kb) mask_rows_above(s[kb], last - kb * 32 - 4 * hh);
             }
             float mraw = -INFINITY;
 #pragma unroll
@@ -172,7 +169,7 @@ fwd_step_kernel(FwdArgs a) {
                 }
             lsum += ps;
             M::template gemm_t_c<LDT>(acc, vt, 0, s[0], lane);
-            if (nk > 32) M::template gemm_t_c<LDT>(acc, vt, 32, s[1], lane);
+            M::template gemm_t_c<LDT>(acc, vt, 32, s[1], lane);
         }
         if (more) {
             kst.store(Ks[buf ^ 1], tid);

@@ -21,6 +21,25 @@ namespace zz {
 // Key offset (inside a 32-key score block) of C register i in lane half hh.
 __device__ __forceinline__ constexpr int c_row(int i, int hh) { return 8 * (i / 4) + 4 * hh + (i % 4); }
 
+// c_row(i, hh) = c_row0(i) + 4*hh.
+__device__ __forceinline__ constexpr int c_row0(int i) { return 8 * (i / 4) + (i % 4); }
+
+// Masks on a 32-row block in C layout, with a per-lane bound already shifted
+// by the lane half (bound - 4*hh): one compare with an immediate per register,
+// so nothing per register stays live across a loop.
+// Rows c_row(i, hh) > bound get -inf.
+__device__ __forceinline__ void mask_rows_above(f32x16 &x, int bound_hh) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (c_row0(i) > bound_hh) x[i] = -INFINITY;
+}
+// Rows c_row(i, hh) < bound get -inf.
+__device__ __forceinline__ void mask_rows_below(f32x16 &x, int bound_hh) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        if (c_row0(i) < bound_hh) x[i] = -INFINITY;
+}
+
 // Position of row k of a tile inside a transposed LDS row: bits 2 and 3 of k
 // swapped.  With it, the 8 contraction values a lane half needs for one
 // 32x32x16 MFMA (rows 4h..4h+3 and 8+4h..8+4h+3 of a 16-row block, the order
