@@ -164,8 +164,11 @@ bwd_dkv_kernel(BwdArgs a) {
     for (int u = 0; u < nwork; ++u) {
         const int buf = u & 1;
         const TileRec tr = load_const(a.tiles, it.tbeg + u % ntile);
-        const bool more = u + 1 < nwork;
-        if (more) fetch(u + 1);
+        // The next tile's loads fly during this tile.  Fetch and stash run on
+        // every iteration (the last one re-reads its own tile into the unused
+        // buffer), so every load is consumed on every path and no wait for
+        // the loads in flight is needed before the next fetch.
+        fetch(min(u + 1, nwork - 1));
         f32x16 x[NQB];   // wave A: P; wave B: dP
         if (pair_on) {
 #pragma unroll
@@ -236,7 +239,7 @@ bwd_dkv_kernel(BwdArgs a) {
                 }
             }
         }
-        if (more) stash(buf ^ 1);
+        stash(buf ^ 1);
         __syncthreads();
     }
     if (!key_ok) return;
@@ -311,8 +314,11 @@ bwd_dq_kernel(BwdArgs a) {
         ktst.store(KsT, tid);
         vst.store(Vs, tid);
         __syncthreads();
-        if (t + 1 < it.tend) {       // next tile's loads fly during this compute
-            const TileRec tn = load_const(a.tiles, t + 1);
+        {
+            // Next tile's loads fly during this compute; issued on every
+            // iteration (the last re-reads its own tile), so every load is
+            // consumed on every path.
+            const TileRec tn = load_const(a.tiles, min(t + 1, it.tend - 1));
             ktst.load(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
             vst.load(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
         }

@@ -116,9 +116,12 @@ fwd_step_kernel(FwdArgs a) {
         const int buf = (t - it.tbeg) & 1;
         const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
-        const bool more = t + 1 < it.tend;
-        if (more) {                  // next tile's loads fly while this one is computed
-            const TileRec tn = load_const(a.tiles, t + 1);
+        {
+            // Next tile's loads fly while this one is computed.  Load and store
+            // run on every iteration (the last one re-reads its own tile into
+            // the unused buffer), so every load is consumed on every path and
+            // no wait for loads in flight is needed before the next load.
+            const TileRec tn = load_const(a.tiles, min(t + 1, it.tend - 1));
             kst.load(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
             vst.load(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
         }
@@ -171,10 +174,8 @@ fwd_step_kernel(FwdArgs a) {
             M::template gemm_t_c<LDT>(acc, vt, 0, s[0], lane);
             M::template gemm_t_c<LDT>(acc, vt, 32, s[1], lane);
         }
-        if (more) {
-            kst.store(Ks[buf ^ 1], tid);
-            vst.store(Vt[buf ^ 1], tid);
-        }
+        kst.store(Ks[buf ^ 1], tid);
+        vst.store(Vt[buf ^ 1], tid);
         __syncthreads();
     }
     if (!row_ok) return;

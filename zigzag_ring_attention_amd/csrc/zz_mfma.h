@@ -161,40 +161,33 @@ __device__ __forceinline__ const char *tile_base(const T *g, int64_t row0, int h
 // A tile of ROWS rows x D columns of a [*, H, D] tensor (one head), staged
 // global -> registers -> LDS by NT threads.  Issuing the global loads for the
 // next tile before computing on the current one hides their latency.
-// Rows past nrows are zero-filled (no read past the end of a chunk).
+// Rows past nrows (a ragged tile) re-read row nrows-1, so every load stays
+// inside the tile's chunk and the code has no branch; the kernels give those
+// rows zero weight (masked scores, or an infinite LSE).
 template <typename T, int D, int ROWS, int NT> struct TileStage {
     static constexpr int EPV = 16 / sizeof(T);   // elements per 16-byte chunk
     static constexpr int CPR = D / EPV;          // chunks per row
     static constexpr int N = ROWS * CPR / NT;    // chunks per thread
     static_assert(N >= 1 && (ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
     static constexpr int LD = RowLayout<T, D>::LD;
-    int4 r[N];
-    uint32_t voff[N];   // byte offset of this thread's chunks from the tile base
+    i32x4 r[N];
+    uint32_t rstride;   // bytes between consecutive rows (wave-uniform)
 
-    __device__ __forceinline__ void init(int heads, int tid) {
+    // Chunk c = tid + i*NT is row c / CPR, elements (c % CPR)*EPV.. of it.
+    __device__ __forceinline__ void init(int heads, int tid) { rstride = (uint32_t)(heads * D * sizeof(T)); }
+    __device__ __forceinline__ void load(const char *base, int nrows, int tid) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int c = tid + i * NT, row = c / CPR, e = (c % CPR) * EPV;
-            voff[i] = (uint32_t)((row * heads * D + e) * sizeof(T));
-        }
-    }
-    __device__ __forceinline__ void load(const char *base, int nrows, int tid) {
-        if (nrows == ROWS) {
-#pragma unroll
-            for (int i = 0; i < N; ++i) r[i] = *reinterpret_cast<const int4 *>(base + voff[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int row = (tid + i * NT) / CPR;
-                r[i] = row < nrows ? *reinterpret_cast<const int4 *>(base + voff[i]) : int4{0, 0, 0, 0};
-            }
+            const int c = tid + i * NT;
+            const uint32_t rr = (uint32_t)min(c / CPR, nrows - 1);
+            r[i] = *reinterpret_cast<const i32x4 *>(base + rr * rstride + (uint32_t)((c % CPR) * 16));
         }
     }
     __device__ __forceinline__ void store(T *lds, int tid) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int c = tid + i * NT, row = c / CPR, e = (c % CPR) * EPV;
-            *reinterpret_cast<int4 *>(lds + row * LD + e) = r[i];
+            const int c = tid + i * NT, e = (c % CPR) * EPV;
+            *reinterpret_cast<i32x4 *>(lds + (c / CPR) * LD + e) = r[i];
         }
     }
 };
@@ -218,8 +211,7 @@ template <typename T, int D, int ROWS, int NT, int RPU = 4> struct TileStageT {
     static_assert(ROWS % 16 == 0, "row count must be a multiple of 16");
     static_assert(CPR % 4 == 0, "column groups must come in fours");
     static_assert(RPU == 4 || RPU == 2, "2 or 4 rows per unit");
-    int4 r[N][RPU];
-    uint32_t voff[N];   // byte offset of row RPU*m, column group cg from the tile base
+    i32x4 r[N][RPU];
     uint32_t rstride;   // bytes between consecutive rows (wave-uniform)
 
     // unit -> (row unit m, column group cg)
@@ -227,32 +219,19 @@ template <typename T, int D, int ROWS, int NT, int RPU = 4> struct TileStageT {
         m = (u / 4) % NQ;
         cg = (u / (4 * NQ)) * 4 + u % 4;
     }
-    __device__ __forceinline__ void init(int heads, int tid) {
-        rstride = (uint32_t)(heads * D * sizeof(T));
+    __device__ __forceinline__ void init(int heads, int tid) { rstride = (uint32_t)(heads * D * sizeof(T)); }
+    // Rows past nrows re-read row nrows-1 (see TileStage).
+    __device__ __forceinline__ void load(const char *base, int nrows, int tid) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
+            const int u = tid + i * NT;
+            if (UNITS % NT != 0 && u >= UNITS) continue;
             int m, cg;
-            unit(tid + i * NT, m, cg);
-            voff[i] = (uint32_t)(RPU * m) * rstride + (uint32_t)(cg * EPV * sizeof(T));
-        }
-    }
-    __device__ __forceinline__ void load(const char *base, int nrows, int tid) {
-        if (nrows == ROWS && UNITS % NT == 0) {
+            unit(u, m, cg);
 #pragma unroll
-            for (int i = 0; i < N; ++i)
-#pragma unroll
-                for (int j = 0; j < RPU; ++j) r[i][j] = *reinterpret_cast<const int4 *>(base + j * rstride + voff[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int u = tid + i * NT;
-                int m, cg;
-                unit(u, m, cg);
-#pragma unroll
-                for (int j = 0; j < RPU; ++j)
-                    r[i][j] = (u < UNITS && RPU * m + j < nrows)
-                                  ? *reinterpret_cast<const int4 *>(base + j * rstride + voff[i])
-                                  : int4{0, 0, 0, 0};
+            for (int j = 0; j < RPU; ++j) {
+                const uint32_t rr = (uint32_t)min(RPU * m + j, nrows - 1);
+                r[i][j] = *reinterpret_cast<const i32x4 *>(base + rr * rstride + (uint32_t)(cg * 16));
             }
         }
     }
@@ -266,9 +245,12 @@ template <typename T, int D, int ROWS, int NT, int RPU = 4> struct TileStageT {
             int m, cg;
             unit(u, m, cg);
 #pragma unroll
-            for (int j = 0; j < RPU; ++j) *reinterpret_cast<int4 *>(lds + (RPU * m + j) * RL::LD + cg * EPV) = r[i][j];
+            for (int j = 0; j < RPU; ++j) *reinterpret_cast<i32x4 *>(lds + (RPU * m + j) * RL::LD + cg * EPV) = r[i][j];
         }
     }
+    // 32-bit word d of a 16-byte chunk (d is a compile-time constant after
+    // unrolling; no address is taken, so the chunk stays in registers).
+    static __device__ __forceinline__ uint32_t word(const i32x4 &v, int d) { return (uint32_t)v[d]; }
     __device__ __forceinline__ void store(T *ldsT, int tid) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
@@ -277,46 +259,29 @@ template <typename T, int D, int ROWS, int NT, int RPU = 4> struct TileStageT {
             int m, cg;
             unit(u, m, cg);
             const int pos = tperm(RPU * m);
-            const uint32_t *w0 = reinterpret_cast<const uint32_t *>(&r[i][0]);
-            const uint32_t *w1 = reinterpret_cast<const uint32_t *>(&r[i][1]);
-            if constexpr (sizeof(T) == 2 && RPU == 4) {
-                const uint32_t *w2 = reinterpret_cast<const uint32_t *>(&r[i][2]);
-                const uint32_t *w3 = reinterpret_cast<const uint32_t *>(&r[i][3]);
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    uint2 lo, hi;   // column 2d (low halves) and 2d+1 (high halves), rows 4m..4m+3
-                    lo.x = (w0[d] & 0xffffu) | (w1[d] << 16);
-                    lo.y = (w2[d] & 0xffffu) | (w3[d] << 16);
-                    hi.x = (w0[d] >> 16) | (w1[d] & 0xffff0000u);
-                    hi.y = (w2[d] >> 16) | (w3[d] & 0xffff0000u);
-                    *reinterpret_cast<uint2 *>(ldsT + (cg * EPV + 2 * d) * LDT + pos) = lo;
-                    *reinterpret_cast<uint2 *>(ldsT + (cg * EPV + 2 * d + 1) * LDT + pos) = hi;
-                }
-            } else if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const uint32_t lo = (w0[d] & 0xffffu) | (w1[d] << 16);
-                    const uint32_t hi = (w0[d] >> 16) | (w1[d] & 0xffff0000u);
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t w0 = word(r[i][0], d), w1 = word(r[i][1], d);
+                if constexpr (sizeof(T) == 2 && RPU == 4) {
+                    const uint32_t w2 = word(r[i][2], d), w3 = word(r[i][3], d);
+                    u32x2 lo, hi;   // column 2d (low halves) and 2d+1 (high halves), rows 4m..4m+3
+                    lo[0] = (w0 & 0xffffu) | (w1 << 16);
+                    lo[1] = (w2 & 0xffffu) | (w3 << 16);
+                    hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
+                    hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+                    *reinterpret_cast<u32x2 *>(ldsT + (cg * EPV + 2 * d) * LDT + pos) = lo;
+                    *reinterpret_cast<u32x2 *>(ldsT + (cg * EPV + 2 * d + 1) * LDT + pos) = hi;
+                } else if constexpr (sizeof(T) == 2) {
+                    const uint32_t lo = (w0 & 0xffffu) | (w1 << 16);
+                    const uint32_t hi = (w0 >> 16) | (w1 & 0xffff0000u);
                     *reinterpret_cast<uint32_t *>(ldsT + (cg * EPV + 2 * d) * LDT + pos) = lo;
                     *reinterpret_cast<uint32_t *>(ldsT + (cg * EPV + 2 * d + 1) * LDT + pos) = hi;
-                }
-            } else if constexpr (RPU == 4) {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    int4 col;
-                    col.x = reinterpret_cast<const int *>(&r[i][0])[d];
-                    col.y = reinterpret_cast<const int *>(&r[i][1])[d];
-                    col.z = reinterpret_cast<const int *>(&r[i][2])[d];
-                    col.w = reinterpret_cast<const int *>(&r[i][3])[d];
-                    *reinterpret_cast<int4 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
-                }
-            } else {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    int2 col;
-                    col.x = reinterpret_cast<const int *>(&r[i][0])[d];
-                    col.y = reinterpret_cast<const int *>(&r[i][1])[d];
-                    *reinterpret_cast<int2 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
+                } else if constexpr (RPU == 4) {
+                    const u32x4 col = {w0, w1, word(r[i][2], d), word(r[i][3], d)};
+                    *reinterpret_cast<u32x4 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
+                } else {
+                    const u32x2 col = {w0, w1};
+                    *reinterpret_cast<u32x2 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
                 }
             }
         }
