@@ -28,6 +28,9 @@ namespace zz {
 namespace {
 
 constexpr int kThreads = 256;
+// s_waitcnt immediate that waits for vmcnt = 0 only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others at their maximum).
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdArgs {
@@ -77,16 +80,20 @@ constexpr int kDkvThreads = 512;
 // (half of what one wave doing everything would hold), so two waves fit per
 // SIMD, and the two roles of a pair share a SIMD and overlap their matrix
 // and vector work.  Q and dO tiles are staged twice (row-major for S and dP,
-// transposed for dK^T and dV^T) and double-buffered with register prefetch.
+// transposed for dK^T and dV^T) and double-buffered; the A waves load the
+// tile after next into registers and write the next one to LDS while the B
+// waves form dS.
 template <typename T, int D>
 __global__ void __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkv_kernel(BwdArgs a) {
     constexpr int kQT = q_tile<T, D>();
     constexpr int NQB = kQT / 32;
     using M = Mfma<T, D>;
-    using TStage = TileStageT<T, D, kQT, kDkvThreads, 2>;
+    // Staged by the A waves: waves 0-1 take Q, waves 2-3 take dO.
+    using TStage = TileStageT<T, D, kQT, kDkvThreads / 4>;
     constexpr int LD = M::LD;
     constexpr int LDT = TStage::LDT;
+    constexpr int SLOTS = TStage::NQ;
     constexpr int NB = D / 32;
     __shared__ __attribute__((aligned(16))) T Qs[2][kQT * LD];
     __shared__ __attribute__((aligned(16))) T Ds[2][kQT * LD];
@@ -131,16 +138,16 @@ bwd_dkv_kernel(BwdArgs a) {
     // Walk (query head of the group) x (listed query tile) as one sequence.
     const int ntile = it.tend - it.tbeg;
     const int nwork = G * ntile;
-    TStage qt, dt;   // one load each feeds both the row-major and the transposed copy
-    qt.init(a.hq, tid);
-    dt.init(a.hq, tid);
+    TStage st;   // one load feeds both the row-major and the transposed copy
+    st.init(a.hq);
+    const bool stage_q = wave < 2;               // wave-uniform
+    const int st_t = tid % (kDkvThreads / 4);
     float lse_r = 0.0f, dlt_r = 0.0f;
     auto fetch = [&](int u) {
         const int h = kvh * G + u / ntile;
         const TileRec tn = load_const(a.tiles, it.tbeg + u % ntile);
         const int nq = tn.b1 - tn.b0;
-        qt.load(tile_base<T, D>(q, qrow0 + tn.b0, a.hq, h), nq, tid);
-        dt.load(tile_base<T, D>(dout, qrow0 + tn.b0, a.hq, h), nq, tid);
+        st.load(tile_base<T, D>(stage_q ? q : dout, qrow0 + tn.b0, a.hq, h), nq, st_t);
         if (tid < kQT) {
             const bool ok = tid < nq;
             // rows past the tile get LSE = +inf, so their P (and dS) is exactly 0
@@ -149,35 +156,43 @@ bwd_dkv_kernel(BwdArgs a) {
         }
     };
     auto stash = [&](int buf) {
-        qt.store_rows(Qs[buf], tid);
-        dt.store_rows(Ds[buf], tid);
-        qt.store(QsT[buf], tid);
-        dt.store(DsT[buf], tid);
+        st.store_rows(stage_q ? Qs[buf] : Ds[buf], st_t);
+        st.store(stage_q ? QsT[buf] : DsT[buf], st_t);
         if (tid < kQT) {
             lse_s[buf][tid] = lse_r * kLog2e;
             dlt_s[buf][tid] = dlt_r;
         }
     };
-    fetch(0);
-    stash(0);
+    if (role_a) {
+        fetch(0);
+        stash(0);
+        fetch(min(1, nwork - 1));
+    }
+    // Wait for every load so far (the key-side operand included) before the
+    // loop: otherwise the wait for the operand lands inside the loop, before
+    // the first product, where the counter also covers the tile loads in
+    // flight.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     for (int u = 0; u < nwork; ++u) {
         const int buf = u & 1;
         const TileRec tr = load_const(a.tiles, it.tbeg + u % ntile);
-        // The next tile's loads fly during this tile.  Fetch and stash run on
-        // every iteration (the last one re-reads its own tile into the unused
-        // buffer), so every load is consumed on every path and no wait for
-        // the loads in flight is needed before the next fetch.
-        fetch(min(u + 1, nwork - 1));
         f32x16 x[NQB];   // wave A: P; wave B: dP
         if (pair_on) {
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
+            for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) x[qb][i] = 0.0f;
-                M::gemm_rows_lds(x[qb], role_a ? Qs[buf] : Ds[buf], qb * 32 + (lane & 31), op, hh);
-            }
+            // Wave A issues its score products at raised priority, so they
+            // finish first and its exponentials overlap the dP products of
+            // wave B on the same SIMD.
+            if (role_a) __builtin_amdgcn_s_setprio(1);
+            if constexpr (NQB == 2)
+                M::gemm_rows_lds2(x[0], x[1], role_a ? Qs[buf] : Ds[buf], lane & 31, 32 + (lane & 31), op, hh);
+            else
+                M::gemm_rows_lds(x[0], role_a ? Qs[buf] : Ds[buf], lane & 31, op, hh);
             if (role_a) {
+                __builtin_amdgcn_s_setprio(0);
                 const float *ls = lse_s[buf];
                 // Only partial (diagonal) tiles need a mask: query rows past a
                 // ragged tile have P = 0 through their LSE, and the columns of
@@ -210,11 +225,22 @@ bwd_dkv_kernel(BwdArgs a) {
             }
         }
         __syncthreads();   // P of every pair is in LDS
+        if (role_a) {
+            // The A waves stage the tiles.  Tile u+1 (loaded during the
+            // previous tile) goes to the other buffer, whose last reader
+            // finished before the barrier that ended the previous tile, while
+            // the B waves start on dS; then the loads of tile u+2 are issued.
+            // Both run on every iteration (past the end they re-read the last
+            // tile into the unused buffer), so every load is consumed on every
+            // path and no wait is needed before a fetch.
+            stash(buf ^ 1);
+            fetch(min(u + 2, nwork - 1));
+        }
         if (pair_on) {
             if (role_a) {
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb)
-                    M::template gemm_t_c<LDT>(acc, DsT[buf], qb * 32, x[qb], lane);
+                    M::template gemm_t_c<LDT, SLOTS>(acc, DsT[buf], qb * 32, x[qb], lane);
             } else {
                 const float *dl = dlt_s[buf];
 #pragma unroll
@@ -235,11 +261,10 @@ bwd_dkv_kernel(BwdArgs a) {
                             x[qb][i] = static_cast<float>(pv[e]) * (x[qb][i] - dv);
                         }
                     }
-                    M::template gemm_t_c<LDT>(acc, QsT[buf], qb * 32, x[qb], lane);
+                    M::template gemm_t_c<LDT, SLOTS>(acc, QsT[buf], qb * 32, x[qb], lane);
                 }
             }
         }
-        stash(buf ^ 1);
         __syncthreads();
     }
     if (!key_ok) return;
@@ -255,10 +280,12 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_DQ_WAVES)))
 bwd_dq_kernel(BwdArgs a) {
     using M = Mfma<T, D>;
-    using RStage = TileStage<T, D, kKT, kThreads>;
-    using TStage = TileStageT<T, D, kKT, kThreads>;
+    // Waves 0-1 stage K (row-major and transposed copies from one load),
+    // waves 2-3 stage V (row-major).
+    using Stage = TileStageT<T, D, kKT, kThreads / 2>;
     constexpr int LD = M::LD;
-    constexpr int LDT = TStage::LDT;
+    constexpr int LDT = Stage::LDT;
+    constexpr int SLOTS = Stage::NQ;
     constexpr int NB = D / 32;
     // K row-major (S^T = K Q^T), K transposed (dQ^T += K^T dS^T), V row-major
     // (dP^T = V dO^T).
@@ -266,7 +293,8 @@ bwd_dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) T KsT[D * LDT];
     __shared__ __attribute__((aligned(16))) T Vs[kKT * LD];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     int item_ix, head;
     block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
     const int kvh = head / (a.hq / a.hkv);
@@ -297,30 +325,31 @@ bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
-    RStage vst;
-    TStage ktst;   // one load of K feeds both its row-major and transposed copies
-    ktst.init(a.hkv, tid);
-    vst.init(a.hkv, tid);
-    {
-        const TileRec tr0 = load_const(a.tiles, it.tbeg);
-        ktst.load(tile_base<T, D>(k, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
-        vst.load(tile_base<T, D>(v, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
-    }
+    Stage st;
+    st.init(a.hkv);
+    const bool stage_k = wave < 2;               // wave-uniform
+    const int st_t = tid % (kThreads / 2);
+    auto fetch = [&](int t) {
+        const TileRec tn = load_const(a.tiles, t);
+        st.load(tile_base<T, D>(stage_k ? k : v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, st_t);
+    };
+    fetch(it.tbeg);
     for (int t = it.tbeg; t < it.tend; ++t) {
         const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
         __syncthreads();
-        ktst.store_rows(Ks, tid);
-        ktst.store(KsT, tid);
-        vst.store(Vs, tid);
+        if (stage_k) {
+            st.store_rows(Ks, st_t);
+            st.store(KsT, st_t);
+        } else {
+            st.store_rows(Vs, st_t);
+        }
         __syncthreads();
         {
             // Next tile's loads fly during this compute; issued on every
             // iteration (the last re-reads its own tile), so every load is
             // consumed on every path.
-            const TileRec tn = load_const(a.tiles, min(t + 1, it.tend - 1));
-            ktst.load(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
-            vst.load(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
+            fetch(min(t + 1, it.tend - 1));
         }
         if (!wave_on) continue;
 #pragma unroll
@@ -340,7 +369,7 @@ bwd_dq_kernel(BwdArgs a) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
                 dp[i] = p * (dp[i] - dlt);
             }
-            M::template gemm_t_c<LDT>(acc, KsT, kb * 32, dp, lane);
+            M::template gemm_t_c<LDT, SLOTS>(acc, KsT, kb * 32, dp, lane);
         }
     }
     if (!row_ok) return;

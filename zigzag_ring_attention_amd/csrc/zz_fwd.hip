@@ -50,16 +50,19 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_FWD_WAVES)))
 fwd_step_kernel(FwdArgs a) {
     using M = Mfma<T, D>;
-    using VStage = TileStageT<T, D, kBN, kThreads>;
+    // Waves 0-1 stage V (its transposed copy), waves 2-3 stage K (row-major).
+    using Stage = TileStageT<T, D, kBN, kThreads / 2>;
     constexpr int LD = M::LD;
-    constexpr int LDT = VStage::LDT;
+    constexpr int LDT = Stage::LDT;
+    constexpr int SLOTS = Stage::NQ;
     constexpr int NB = D / 32;   // 32-wide head-dim blocks of O^T
     // Double-buffered: K row-major (A operand of S^T = K Q^T), V transposed
     // (A operand of O^T = V^T P^T).  One barrier per tile.
     __shared__ __attribute__((aligned(16))) T Ks[2][kBN * LD];
     __shared__ __attribute__((aligned(16))) T Vt[2][D * LDT];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
+    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     int item_ix, head;
     block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
     const int kvh = head / (a.hq / a.hkv);
@@ -100,41 +103,43 @@ fwd_step_kernel(FwdArgs a) {
     float m = -INFINITY, lsum = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
-    TileStage<T, D, kBN, kThreads> kst;
-    VStage vst;
-    kst.init(a.hkv, tid);
-    vst.init(a.hkv, tid);
-    {
-        const TileRec tr0 = load_const(a.tiles, it.tbeg);
-        kst.load(tile_base<T, D>(k, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
-        vst.load(tile_base<T, D>(v, kv_row0 + tr0.b0, a.hkv, kvh), tr0.b1 - tr0.b0, tid);
-        kst.store(Ks[0], tid);
-        vst.store(Vt[0], tid);
-    }
+    Stage st;
+    st.init(a.hkv);
+    const bool stage_v = wave < 2;               // wave-uniform
+    const int st_t = tid % (kThreads / 2);
+    auto fetch = [&](int t) {
+        const TileRec tn = load_const(a.tiles, t);
+        st.load(tile_base<T, D>(stage_v ? v : k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, st_t);
+    };
+    auto stash = [&](int buf) {
+        if (stage_v) st.store(Vt[buf], st_t);
+        else st.store_rows(Ks[buf], st_t);
+    };
+    fetch(it.tbeg);
+    stash(0);
+    fetch(min(it.tbeg + 1, it.tend - 1));
     __syncthreads();
     for (int t = it.tbeg; t < it.tend; ++t) {
         const int buf = (t - it.tbeg) & 1;
         const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
-        {
-            // Next tile's loads fly while this one is computed.  Load and store
-            // run on every iteration (the last one re-reads its own tile into
-            // the unused buffer), so every load is consumed on every path and
-            // no wait for loads in flight is needed before the next load.
-            const TileRec tn = load_const(a.tiles, min(t + 1, it.tend - 1));
-            kst.load(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
-            vst.load(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, tid);
-        }
+        // Tile t+1, loaded during the previous tile, goes to the other buffer
+        // (its last reader finished before the barrier that ended the
+        // previous tile), then the loads of tile t+2 are issued; both overlap
+        // this tile's compute.  They run on every iteration (past the end they
+        // re-read the last tile into the unused buffer), so every load is
+        // consumed on every path and no wait is needed before a load.
+        stash(buf ^ 1);
+        fetch(min(t + 2, it.tend - 1));
         if (wave_on) {
             const T *ks = Ks[buf];
             const T *vt = Vt[buf];
             f32x16 s[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[kb][i] = 0.0f;
-                M::gemm_rows_lds(s[kb], ks, kb * 32 + (lane & 31), qop, hh);
-            }
+            M::gemm_rows_lds2(s[0], s[1], ks, lane & 31, 32 + (lane & 31), qop, hh);
             // mask (partial and ragged tiles only): key kk is kept iff
             // kk < nk and, in a partial tile, kk <= qq + delta
             if (tr.kind != ZZ_TILE_FULL || nk < kBN) {
@@ -171,11 +176,9 @@ fwd_step_kernel(FwdArgs a) {
                     ps += p;
                 }
             lsum += ps;
-            M::template gemm_t_c<LDT>(acc, vt, 0, s[0], lane);
-            M::template gemm_t_c<LDT>(acc, vt, 32, s[1], lane);
+            M::template gemm_t_c<LDT, SLOTS>(acc, vt, 0, s[0], lane);
+            M::template gemm_t_c<LDT, SLOTS>(acc, vt, 32, s[1], lane);
         }
-        kst.store(Ks[buf ^ 1], tid);
-        vst.store(Vt[buf ^ 1], tid);
         __syncthreads();
     }
     if (!row_ok) return;

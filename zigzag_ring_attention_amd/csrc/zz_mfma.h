@@ -8,10 +8,10 @@
 //
 // Scores are formed transposed (S^T = K Q^T), so the C layout puts one query
 // per lane column: the softmax row statistics of a query live in one lane
-// pair (l, l^32), and P^T in C layout is already the B operand of O^T = V^T P^T
-// when the contraction runs over the keys in the order k(e) = 8*(e/4) +
-// 4*(l/32) + e%4 -- the A operand (V^T) is then read from a transposed LDS
-// copy whose rows hold the keys in that order (tperm).
+// pair (l, l^32).  P^T in C layout becomes the B operand of O^T = V^T P^T
+// after one exchange between the lane halves (order_for_b), which puts the
+// keys of a lane half in natural order; the A operand (V^T) is read from a
+// transposed LDS copy whose rows hold the keys in natural order.
 #pragma once
 
 #include "zz_device.h"
@@ -40,11 +40,23 @@ __device__ __forceinline__ void mask_rows_below(f32x16 &x, int bound_hh) {
         if (c_row0(i) < bound_hh) x[i] = -INFINITY;
 }
 
-// Position of row k of a tile inside a transposed LDS row: bits 2 and 3 of k
-// swapped.  With it, the 8 contraction values a lane half needs for one
-// 32x32x16 MFMA (rows 4h..4h+3 and 8+4h..8+4h+3 of a 16-row block, the order
-// c_row produces) sit in 16 contiguous bytes.
-__device__ __forceinline__ constexpr int tperm(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+// Reorder a 32-row block in C layout into B-operand order: afterwards lane
+// half hh holds rows 16*h + 8*hh + e in register 8*h + e (h = 0, 1; e = 0..7),
+// the contraction order of a 32x32x16 MFMA over natural rows.  In C layout
+// half hh holds rows 16*h + 4*hh + {0..3, 8..11}; one permlane32 swap per
+// register pair (j, j+4) exchanges rows 4..7 of half 0 with rows 8..11 of
+// half 1.
+__device__ __forceinline__ void order_for_b(f32x16 &x) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[8 * h + j]), __float_as_uint(x[8 * h + 4 + j]),
+                                                      false, false);
+            x[8 * h + j] = __uint_as_float(r[0]);       // lanes 0-31 keep, 32-63 get rows 8..11 of half 0
+            x[8 * h + 4 + j] = __uint_as_float(r[1]);   // lanes 0-31 get rows 4..7 of half 1, 32-63 keep
+        }
+}
 
 // Exchange a value with lane l^32.
 __device__ __forceinline__ float swap_halves(float x, int lane) {
@@ -91,25 +103,76 @@ template <int D> struct Mfma<bf16, D> {
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[ks], acc, 0, 0, 0);
         }
     }
-    // acc[cb] += X^T * P for a tile X stored transposed in LDS (row = column of
-    // X, LDT elements per row, X rows permuted by tperm): X rows r0..r0+31
-    // against a 32 x 32 block P in C layout.  16-byte reads, two MFMAs per
-    // 32 contraction rows and 32 columns.
-    template <int LDT>
+    // Two chains over the same operand op: acc0 += rows row0.. x op and
+    // acc1 += rows row1.. x op.  The LDS operands of a step are read one step
+    // ahead, and the two chains alternate, so neither the LDS latency nor the
+    // accumulator dependency stalls the matrix unit.
+    static __device__ __forceinline__ void gemm_rows_lds2(f32x16 &acc0, f32x16 &acc1, const bf16 *tile, int row0,
+                                                          int row1, const Op (&op)[KS], int hh) {
+        bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row0, 8 * hh));
+        bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row1, 8 * hh));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 n0 = a0, n1 = a1;
+            if (ks + 1 < KS) {
+                n0 = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row0, 16 * (ks + 1) + 8 * hh));
+                n1 = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row1, 16 * (ks + 1) + 8 * hh));
+            }
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, op[ks], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, op[ks], acc1, 0, 0, 0);
+            a0 = n0;
+            a1 = n1;
+        }
+    }
+    // Two chains with their own tiles and operands (same rows).
+    static __device__ __forceinline__ void gemm_rows_lds_pair(f32x16 &acc0, const bf16 *tile0, const Op (&op0)[KS],
+                                                              f32x16 &acc1, const bf16 *tile1, const Op (&op1)[KS],
+                                                              int row, int hh) {
+        bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(tile0 + RL::at(row, 8 * hh));
+        bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(tile1 + RL::at(row, 8 * hh));
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            bf16x8 n0 = a0, n1 = a1;
+            if (ks + 1 < KS) {
+                n0 = *reinterpret_cast<const bf16x8 *>(tile0 + RL::at(row, 16 * (ks + 1) + 8 * hh));
+                n1 = *reinterpret_cast<const bf16x8 *>(tile1 + RL::at(row, 16 * (ks + 1) + 8 * hh));
+            }
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, op0[ks], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, op1[ks], acc1, 0, 0, 0);
+            a0 = n0;
+            a1 = n1;
+        }
+    }
+    // acc[cb] += X^T * P for a tile X stored transposed in LDS (row = column
+    // of X, LDT elements per row, X rows in natural order): X rows r0..r0+31
+    // against a 32 x 32 block P in C layout.  16-byte reads, two MFMAs per 32
+    // contraction rows and 32 columns; all LDS operands of the block are read
+    // before the first MFMA, so only the first read's latency shows.
+    // The transposed tile is a TileStageT copy: SLOTS 16-byte slots per row,
+    // swizzled by TileStageT::tpos.
+    template <int LDT, int SLOTS>
     static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const bf16 *tileT, int r0,
                                                     const f32x16 &p, int lane) {
         const int hh = lane >> 5;
+        bf16x8 a[2][D / 32];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const int row = 32 * cb + (lane & 31);
+                const int slot = ((r0 + 16 * half + 8 * hh) / 8) ^ ((row >> 4) & (SLOTS - 1));
+                a[half][cb] = *reinterpret_cast<const bf16x8 *>(tileT + row * LDT + 8 * slot);
+            }
+        f32x16 pb = p;
+        order_for_b(pb);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             bf16x8 b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = to_bf16(p[8 * half + e]);
+            for (int e = 0; e < 8; ++e) b[e] = to_bf16(pb[8 * half + e]);
 #pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tileT + (32 * cb + (lane & 31)) * LDT + r0 +
-                                                                   16 * half + 8 * hh);
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[cb], 0, 0, 0);
-            }
+            for (int cb = 0; cb < D / 32; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[half][cb], b, acc[cb], 0, 0, 0);
         }
     }
 };
@@ -135,17 +198,30 @@ template <int D> struct Mfma<float, D> {
         for (int ks = 0; ks < KS; ++ks)
             acc = __builtin_amdgcn_mfma_f32_32x32x2f32(tile[RL::at(row, 2 * ks + hh)], op[ks], acc, 0, 0, 0);
     }
-    template <int LDT>
+    static __device__ __forceinline__ void gemm_rows_lds2(f32x16 &acc0, f32x16 &acc1, const float *tile, int row0,
+                                                          int row1, const Op (&op)[KS], int hh) {
+        gemm_rows_lds(acc0, tile, row0, op, hh);
+        gemm_rows_lds(acc1, tile, row1, op, hh);
+    }
+    static __device__ __forceinline__ void gemm_rows_lds_pair(f32x16 &acc0, const float *tile0, const Op (&op0)[KS],
+                                                              f32x16 &acc1, const float *tile1, const Op (&op1)[KS],
+                                                              int row, int hh) {
+        gemm_rows_lds(acc0, tile0, row, op0, hh);
+        gemm_rows_lds(acc1, tile1, row, op1, hh);
+    }
+    template <int LDT, int SLOTS>
     static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const float *tileT, int r0,
                                                     const f32x16 &p, int lane) {
         const int hh = lane >> 5;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int pos = r0 + tperm(c_row(i, hh));
+            const int pos = r0 + c_row(i, hh);
 #pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb)
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(tileT[(32 * cb + (lane & 31)) * LDT + pos], p[i],
-                                                                acc[cb], 0, 0, 0);
+            for (int cb = 0; cb < D / 32; ++cb) {
+                const int row = 32 * cb + (lane & 31);
+                const int at = (((pos / 4) ^ ((row >> 4) & (SLOTS - 1))) * 4) + pos % 4;
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(tileT[row * LDT + at], p[i], acc[cb], 0, 0, 0);
+            }
         }
     }
 };
@@ -193,96 +269,98 @@ template <typename T, int D, int ROWS, int NT> struct TileStage {
 };
 
 // A tile of ROWS rows x D columns of a [*, H, D] tensor (one head), staged
-// into LDS transposed: LDS row c holds column c of the tile, the tile rows
-// placed at tperm(row).  Each thread gathers RPU (4 or 2) consecutive rows x
-// one 16-byte column group, regroups them in registers, and writes RPU
-// consecutive rows per LDS column.  The same registers also give the
-// row-major copy (store_rows).  Lanes are laid out as 4 column groups x the
-// row units x the rest of the column groups, which keeps the stores of 16
-// lanes on distinct (RPU 4) or at most two-way shared (RPU 2) bank groups.
-template <typename T, int D, int ROWS, int NT, int RPU = 4> struct TileStageT {
-    static constexpr int EPV = 16 / sizeof(T);
+// global -> registers -> LDS as a row-major copy (RowLayout) and a transposed
+// copy: LDS row c holds column c of the tile, the tile rows in natural order
+// in 16-byte groups whose slots are XOR-swizzled by the row (tpos), with
+// LDT = ROWS + 16 bytes of padding per row.  A unit is RU = 16/sizeof(T)
+// consecutive rows x one 16-byte column group; its RU x RU block is
+// transposed in registers, so both copies are written with 16-byte stores
+// (narrower LDS stores run far below the 16-byte ones).  Units are dealt to
+// the NT staging threads column-group first, so each global load of a wave
+// reads whole rows and the row-major stores of 16 lanes fill consecutive
+// 16-byte slots; the swizzle does the same for the transposed stores, whose
+// 16 lanes would otherwise land on two bank groups.  Rows past nrows re-read
+// row nrows-1 (see TileStage).
+template <typename T, int D, int ROWS, int NT> struct TileStageT {
+    static constexpr int EPV = 16 / sizeof(T);   // elements per 16-byte chunk
+    static constexpr int RU = EPV;               // rows per unit
     static constexpr int CPR = D / EPV;          // 16-byte column groups
-    static constexpr int NQ = ROWS / RPU;        // row units
+    static constexpr int NQ = ROWS / RU;         // row units
     static constexpr int UNITS = NQ * CPR;
     static constexpr int N = (UNITS + NT - 1) / NT;
-    static constexpr int PADT = 16 / sizeof(T);  // 16 bytes of padding per LDS row
-    static constexpr int LDT = ROWS + PADT;
-    static_assert(ROWS % 16 == 0, "row count must be a multiple of 16");
-    static_assert(CPR % 4 == 0, "column groups must come in fours");
-    static_assert(RPU == 4 || RPU == 2, "2 or 4 rows per unit");
-    i32x4 r[N][RPU];
+    static constexpr int LDT = ROWS + EPV;       // transposed row stride (elements)
+    static_assert(ROWS % RU == 0, "rows must split into units");
+    static_assert((NQ & (NQ - 1)) == 0, "row units must be a power of two");
+    i32x4 r[N][RU];
     uint32_t rstride;   // bytes between consecutive rows (wave-uniform)
 
     // unit -> (row unit m, column group cg)
     static __device__ __forceinline__ void unit(int u, int &m, int &cg) {
-        m = (u / 4) % NQ;
-        cg = (u / (4 * NQ)) * 4 + u % 4;
+        m = u / CPR;
+        cg = u % CPR;
     }
-    __device__ __forceinline__ void init(int heads, int tid) { rstride = (uint32_t)(heads * D * sizeof(T)); }
-    // Rows past nrows re-read row nrows-1 (see TileStage).
-    __device__ __forceinline__ void load(const char *base, int nrows, int tid) {
+    // Element offset of tile row `pos` inside transposed LDS row `row`: the
+    // 16-byte slot is XOR-ed with bits 4.. of the row, so 16 consecutive
+    // rows read the same slot conflict-free (odd row stride in slots) and the
+    // 16 rows cg*EPV + c written by 16 lanes spread over all slots.
+    static __device__ __forceinline__ constexpr int tpos(int row, int pos) {
+        return (((pos / EPV) ^ ((row >> 4) & (NQ - 1))) * EPV) + pos % EPV;
+    }
+    __device__ __forceinline__ void init(int heads) { rstride = (uint32_t)(heads * D * sizeof(T)); }
+    // t: this thread's index among the NT staging threads.
+    __device__ __forceinline__ void load(const char *base, int nrows, int t) {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int u = tid + i * NT;
+            const int u = t + i * NT;
             if (UNITS % NT != 0 && u >= UNITS) continue;
             int m, cg;
             unit(u, m, cg);
 #pragma unroll
-            for (int j = 0; j < RPU; ++j) {
-                const uint32_t rr = (uint32_t)min(RPU * m + j, nrows - 1);
+            for (int j = 0; j < RU; ++j) {
+                const uint32_t rr = (uint32_t)min(RU * m + j, nrows - 1);
                 r[i][j] = *reinterpret_cast<const i32x4 *>(base + rr * rstride + (uint32_t)(cg * 16));
             }
         }
     }
-    // Row-major copy of the same rows (the layout of RowLayout).
-    __device__ __forceinline__ void store_rows(T *lds, int tid) const {
+    // Row-major copy (the layout of RowLayout).
+    __device__ __forceinline__ void store_rows(T *lds, int t) const {
         using RL = RowLayout<T, D>;
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int u = tid + i * NT;
+            const int u = t + i * NT;
             if (UNITS % NT != 0 && u >= UNITS) continue;
             int m, cg;
             unit(u, m, cg);
 #pragma unroll
-            for (int j = 0; j < RPU; ++j) *reinterpret_cast<i32x4 *>(lds + (RPU * m + j) * RL::LD + cg * EPV) = r[i][j];
+            for (int j = 0; j < RU; ++j) *reinterpret_cast<i32x4 *>(lds + (RU * m + j) * RL::LD + cg * EPV) = r[i][j];
         }
     }
-    // 32-bit word d of a 16-byte chunk (d is a compile-time constant after
-    // unrolling; no address is taken, so the chunk stays in registers).
-    static __device__ __forceinline__ uint32_t word(const i32x4 &v, int d) { return (uint32_t)v[d]; }
-    __device__ __forceinline__ void store(T *ldsT, int tid) const {
+    // Element c (0..EPV-1) of row j of unit i, as the low bits of a word.
+    __device__ __forceinline__ uint32_t half_of(int i, int j, int c) const {
+        const uint32_t w = (uint32_t)r[i][j][c / 2];
+        return (c & 1) ? (w >> 16) : (w & 0xffffu);
+    }
+    // Transposed copy: column c of the unit's column group is LDS row
+    // cg*EPV + c, the unit's RU rows at positions RU*m .. RU*m+RU-1.
+    __device__ __forceinline__ void store(T *ldsT, int t) const {
 #pragma unroll
         for (int i = 0; i < N; ++i) {
-            const int u = tid + i * NT;
+            const int u = t + i * NT;
             if (UNITS % NT != 0 && u >= UNITS) continue;
             int m, cg;
             unit(u, m, cg);
-            const int pos = tperm(RPU * m);
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t w0 = word(r[i][0], d), w1 = word(r[i][1], d);
-                if constexpr (sizeof(T) == 2 && RPU == 4) {
-                    const uint32_t w2 = word(r[i][2], d), w3 = word(r[i][3], d);
-                    u32x2 lo, hi;   // column 2d (low halves) and 2d+1 (high halves), rows 4m..4m+3
-                    lo[0] = (w0 & 0xffffu) | (w1 << 16);
-                    lo[1] = (w2 & 0xffffu) | (w3 << 16);
-                    hi[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-                    hi[1] = (w2 >> 16) | (w3 & 0xffff0000u);
-                    *reinterpret_cast<u32x2 *>(ldsT + (cg * EPV + 2 * d) * LDT + pos) = lo;
-                    *reinterpret_cast<u32x2 *>(ldsT + (cg * EPV + 2 * d + 1) * LDT + pos) = hi;
-                } else if constexpr (sizeof(T) == 2) {
-                    const uint32_t lo = (w0 & 0xffffu) | (w1 << 16);
-                    const uint32_t hi = (w0 >> 16) | (w1 & 0xffff0000u);
-                    *reinterpret_cast<uint32_t *>(ldsT + (cg * EPV + 2 * d) * LDT + pos) = lo;
-                    *reinterpret_cast<uint32_t *>(ldsT + (cg * EPV + 2 * d + 1) * LDT + pos) = hi;
-                } else if constexpr (RPU == 4) {
-                    const u32x4 col = {w0, w1, word(r[i][2], d), word(r[i][3], d)};
-                    *reinterpret_cast<u32x4 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
+            for (int c = 0; c < EPV; ++c) {
+                u32x4 col;
+                if constexpr (sizeof(T) == 2) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) col[k] = half_of(i, 2 * k, c) | (half_of(i, 2 * k + 1, c) << 16);
                 } else {
-                    const u32x2 col = {w0, w1};
-                    *reinterpret_cast<u32x2 *>(ldsT + (cg * EPV + d) * LDT + pos) = col;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) col[k] = (uint32_t)r[i][k][c];
                 }
+                const int row = cg * EPV + c;
+                *reinterpret_cast<u32x4 *>(ldsT + row * LDT + tpos(row, RU * m)) = col;
             }
         }
     }
