@@ -79,26 +79,20 @@ constexpr int kDkvThreads = 512;
 // dK^T += Q^T dS.  Each wave keeps one key-side operand and one accumulator
 // (half of what one wave doing everything would hold), so two waves fit per
 // SIMD, and the two roles of a pair share a SIMD and overlap their matrix
-// and vector work.  Q and dO tiles are staged twice (row-major for S and dP,
-// transposed for dK^T and dV^T) and double-buffered; the A waves load the
-// tile after next into registers and write the next one to LDS while the B
-// waves form dS.
+// and vector work.  Q and dO tiles are staged once, row-major, in double
+// buffers filled by the memory unit while the previous tile is computed; S
+// and dP read their rows, dK^T and dV^T read them transposed.
 template <typename T, int D>
 __global__ void __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkv_kernel(BwdArgs a) {
     constexpr int kQT = q_tile<T, D>();
     constexpr int NQB = kQT / 32;
     using M = Mfma<T, D>;
-    // Staged by the A waves: waves 0-1 take Q, waves 2-3 take dO.
-    using TStage = TileStageT<T, D, kQT, kDkvThreads / 4>;
-    constexpr int LD = M::LD;
-    constexpr int LDT = TStage::LDT;
-    constexpr int SLOTS = TStage::NQ;
+    constexpr int NW = kDkvThreads / 64;
+    using DmaRows = Dma<kQT, M::W, NW>;
     constexpr int NB = D / 32;
-    __shared__ __attribute__((aligned(16))) T Qs[2][kQT * LD];
-    __shared__ __attribute__((aligned(16))) T Ds[2][kQT * LD];
-    __shared__ __attribute__((aligned(16))) T QsT[2][D * LDT];
-    __shared__ __attribute__((aligned(16))) T DsT[2][D * LDT];
+    __shared__ __attribute__((aligned(16))) T Qs[2][kQT * D];
+    __shared__ __attribute__((aligned(16))) T Ds[2][kQT * D];
     __shared__ __attribute__((aligned(16))) float lse_s[2][kQT], dlt_s[2][kQT];
     // P handed from wave A to wave B: fp16 for 16-bit inputs (10-bit mantissa,
     // so the dS that forms dK is close to the one the dQ kernel forms from
@@ -138,45 +132,42 @@ bwd_dkv_kernel(BwdArgs a) {
     // Walk (query head of the group) x (listed query tile) as one sequence.
     const int ntile = it.tend - it.tbeg;
     const int nwork = G * ntile;
-    TStage st;   // one load feeds both the row-major and the transposed copy
-    st.init(a.hq);
-    const bool stage_q = wave < 2;               // wave-uniform
-    const int st_t = tid % (kDkvThreads / 4);
+    // Row-major tiles of Q and dO are copied global -> LDS by the memory
+    // unit, every wave issuing its share (Q^T and dO^T are read from them by
+    // LDS transpose reads); the LSE and delta of a tile go through the
+    // registers of the first kQT threads (rows past the tile get LSE = +inf,
+    // so their P and dS are exactly 0).
     float lse_r = 0.0f, dlt_r = 0.0f;
-    auto fetch = [&](int u) {
+    auto copy_tile = [&](int u, int buf) {
         const int h = kvh * G + u / ntile;
         const TileRec tn = load_const(a.tiles, it.tbeg + u % ntile);
         const int nq = tn.b1 - tn.b0;
-        st.load(tile_base<T, D>(stage_q ? q : dout, qrow0 + tn.b0, a.hq, h), nq, st_t);
-        if (tid < kQT) {
+        if (tid < kQT) {   // issued first: the counter waits below do not cover the copies
             const bool ok = tid < nq;
-            // rows past the tile get LSE = +inf, so their P (and dS) is exactly 0
-            lse_r = ok ? a.lse[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : INFINITY;   // scaled when stashed
+            lse_r = ok ? a.lse[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : INFINITY;   // scaled when stored
             dlt_r = ok ? a.delta[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : 0.0f;
         }
+        const uint32_t rstride = (uint32_t)(a.hq * D * sizeof(T));
+        DmaRows::issue_rows(tile_base<T, D>(q, qrow0 + tn.b0, a.hq, h), rstride, nq, Qs[buf], wave, lane);
+        DmaRows::issue_rows(tile_base<T, D>(dout, qrow0 + tn.b0, a.hq, h), rstride, nq, Ds[buf], wave, lane);
     };
-    auto stash = [&](int buf) {
-        st.store_rows(stage_q ? Qs[buf] : Ds[buf], st_t);
-        st.store(stage_q ? QsT[buf] : DsT[buf], st_t);
+    auto store_stats = [&](int buf) {
         if (tid < kQT) {
             lse_s[buf][tid] = lse_r * kLog2e;
             dlt_s[buf][tid] = dlt_r;
         }
     };
-    if (role_a) {
-        fetch(0);
-        stash(0);
-        fetch(min(1, nwork - 1));
-    }
-    // Wait for every load so far (the key-side operand included) before the
-    // loop: otherwise the wait for the operand lands inside the loop, before
-    // the first product, where the counter also covers the tile loads in
-    // flight.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    copy_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the key-side operand and tile 0 have landed
+    store_stats(0);
     __syncthreads();
     for (int u = 0; u < nwork; ++u) {
         const int buf = u & 1;
         const TileRec tr = load_const(a.tiles, it.tbeg + u % ntile);
+        // Tile u+1 is copied into the other buffer (its last readers finished
+        // before the barrier that ended the previous tile) while this tile is
+        // computed; past the end the copy re-reads the last tile.
+        copy_tile(min(u + 1, nwork - 1), buf ^ 1);
         f32x16 x[NQB];   // wave A: P; wave B: dP
         if (pair_on) {
 #pragma unroll
@@ -225,22 +216,11 @@ bwd_dkv_kernel(BwdArgs a) {
             }
         }
         __syncthreads();   // P of every pair is in LDS
-        if (role_a) {
-            // The A waves stage the tiles.  Tile u+1 (loaded during the
-            // previous tile) goes to the other buffer, whose last reader
-            // finished before the barrier that ended the previous tile, while
-            // the B waves start on dS; then the loads of tile u+2 are issued.
-            // Both run on every iteration (past the end they re-read the last
-            // tile into the unused buffer), so every load is consumed on every
-            // path and no wait is needed before a fetch.
-            stash(buf ^ 1);
-            fetch(min(u + 2, nwork - 1));
-        }
         if (pair_on) {
             if (role_a) {
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb)
-                    M::template gemm_t_c<LDT, SLOTS>(acc, DsT[buf], qb * 32, x[qb], lane);
+                    M::gemm_t_c(acc, Ds[buf], qb * 32, x[qb], lane);
             } else {
                 const float *dl = dlt_s[buf];
 #pragma unroll
@@ -261,10 +241,12 @@ bwd_dkv_kernel(BwdArgs a) {
                             x[qb][i] = static_cast<float>(pv[e]) * (x[qb][i] - dv);
                         }
                     }
-                    M::template gemm_t_c<LDT, SLOTS>(acc, QsT[buf], qb * 32, x[qb], lane);
+                    M::gemm_t_c(acc, Qs[buf], qb * 32, x[qb], lane);
                 }
             }
         }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile u+1 have landed
+        store_stats(buf ^ 1);
         __syncthreads();
     }
     if (!key_ok) return;
@@ -274,24 +256,27 @@ bwd_dkv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dQ
 
-constexpr int kKT = 64;   // keys per streamed tile
+// Keys per streamed tile (must match the planner's dQ tile): halved for fp32
+// with D >= 64 so the double-buffered LDS stage fits.
+template <typename T, int D> constexpr int k_tile() { return (sizeof(T) == 4 && D >= 64) ? 32 : 64; }
+constexpr int kDqThreads = 512;    // eight waves own 32 query rows each
 
+// Query-major: a workgroup owns up to 256 query rows of one head (eight
+// waves of 32) and walks the item's key tiles, with the K and V tiles copied
+// global -> LDS by the memory unit into double buffers (K^T is read from the
+// K tile by LDS transpose reads).
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_DQ_WAVES)))
+__global__ void __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(ZZ_DQ_WAVES)))
 bwd_dq_kernel(BwdArgs a) {
     using M = Mfma<T, D>;
-    // Waves 0-1 stage K (row-major and transposed copies from one load),
-    // waves 2-3 stage V (row-major).
-    using Stage = TileStageT<T, D, kKT, kThreads / 2>;
-    constexpr int LD = M::LD;
-    constexpr int LDT = Stage::LDT;
-    constexpr int SLOTS = Stage::NQ;
+    constexpr int kKT = k_tile<T, D>();
+    constexpr int NW = kDqThreads / 64;
+    using DmaRows = Dma<kKT, M::W, NW>;
     constexpr int NB = D / 32;
-    // K row-major (S^T = K Q^T), K transposed (dQ^T += K^T dS^T), V row-major
-    // (dP^T = V dO^T).
-    __shared__ __attribute__((aligned(16))) T Ks[kKT * LD];
-    __shared__ __attribute__((aligned(16))) T KsT[D * LDT];
-    __shared__ __attribute__((aligned(16))) T Vs[kKT * LD];
+    // K (S^T = K Q^T, and read transposed for dQ^T += K^T dS^T) and V
+    // (dP^T = V dO^T), row-major.
+    __shared__ __attribute__((aligned(16))) T Ks[2][kKT * D];
+    __shared__ __attribute__((aligned(16))) T Vs[2][kKT * D];
 
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -325,52 +310,47 @@ bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
-    Stage st;
-    st.init(a.hkv);
-    const bool stage_k = wave < 2;               // wave-uniform
-    const int st_t = tid % (kThreads / 2);
-    auto fetch = [&](int t) {
+    auto copy_tile = [&](int t, int buf) {
         const TileRec tn = load_const(a.tiles, t);
-        st.load(tile_base<T, D>(stage_k ? k : v, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, st_t);
+        const int nk = tn.b1 - tn.b0;
+        const uint32_t rstride = (uint32_t)(a.hkv * D * sizeof(T));
+        DmaRows::issue_rows(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), rstride, nk, Ks[buf], wave, lane);
+        DmaRows::issue_rows(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), rstride, nk, Vs[buf], wave, lane);
     };
-    fetch(it.tbeg);
+    copy_tile(it.tbeg, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the query-side operands and tile 0 have landed
+    __syncthreads();
     for (int t = it.tbeg; t < it.tend; ++t) {
+        const int buf = (t - it.tbeg) & 1;
         const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
-        __syncthreads();
-        if (stage_k) {
-            st.store_rows(Ks, st_t);
-            st.store(KsT, st_t);
-        } else {
-            st.store_rows(Vs, st_t);
-        }
-        __syncthreads();
-        {
-            // Next tile's loads fly during this compute; issued on every
-            // iteration (the last re-reads its own tile), so every load is
-            // consumed on every path.
-            fetch(min(t + 1, it.tend - 1));
-        }
-        if (!wave_on) continue;
+        // Tile t+1 is copied into the other buffer (its last readers finished
+        // before the barrier that ended the previous tile) while this tile is
+        // computed; past the end the copy re-reads the last tile.
+        copy_tile(min(t + 1, it.tend - 1), buf ^ 1);
+        if (wave_on) {
 #pragma unroll
-        for (int kb = 0; kb < kKT / 32; ++kb) {
-            f32x16 s, dp;
+            for (int kb = 0; kb < kKT / 32; ++kb) {
+                f32x16 s, dp;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
-            M::gemm_rows_lds(s, Ks, kb * 32 + (lane & 31), qop, hh);
-            M::gemm_rows_lds(dp, Vs, kb * 32 + (lane & 31), dop, hh);
-            // mask (partial and ragged tiles only): key kk is kept iff kk < nk
-            // and, in a partial tile, kk <= qq + delta; rows of queries past
-            // the item are never written
-            if (tr.kind != ZZ_TILE_FULL || nk < kKT)
-                mask_rows_above(s, (tr.kind == ZZ_TILE_FULL ? nk - 1 : min(nk - 1, qq + tr.delta)) - kb * 32 - 4 * hh);
+                for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+                M::gemm_rows_lds_pair(s, Ks[buf], qop, dp, Vs[buf], dop, kb * 32 + (lane & 31), hh);
+                // mask (partial and ragged tiles only): key kk is kept iff kk < nk
+                // and, in a partial tile, kk <= qq + delta; rows of queries past
+                // the item are never written
+                if (tr.kind != ZZ_TILE_FULL || nk < kKT)
+                    mask_rows_above(s, (tr.kind == ZZ_TILE_FULL ? nk - 1 : min(nk - 1, qq + tr.delta)) - kb * 32 -
+                                           4 * hh);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
-                dp[i] = p * (dp[i] - dlt);
+                for (int i = 0; i < 16; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
+                    dp[i] = p * (dp[i] - dlt);
+                }
+                M::gemm_t_c(acc, Ks[buf], kb * 32, dp, lane);
             }
-            M::template gemm_t_c<LDT, SLOTS>(acc, KsT, kb * 32, dp, lane);
         }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile t+1 have landed
+        __syncthreads();
     }
     if (!row_ok) return;
     add_row<NB>(a.dq + (zrow * a.hq + head) * D, acc, a.scale, hh, a.accumulate != 0);
@@ -388,7 +368,7 @@ hipError_t launch_t(const zz_plan *p, int rank, int step, BwdArgs a, int which, 
     const Launch Lq = launch_items(p, ZZ_PASS_BWD_DQ, rank, step);
     if ((which & 2) && Lq.n > 0) {
         a.items = Lq.items; a.order = Lq.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DQ); a.nitems = Lq.n;
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(Lq.n * p->hq), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(Lq.n * p->hq), dim3(kDqThreads), 0, st, a);
     }
     return hipGetLastError();
 }

@@ -6,7 +6,9 @@
 // inside one zigzag chunk) x one query head.  Four waves own 32 query rows
 // each.  The workgroup walks the item's listed key tiles of shard
 // j = (rank - step) mod CP -- fully masked tiles were pruned by the planner --
-// staging K and V tiles of up to 64 keys in LDS.  Per tile and wave:
+// with K and V tiles of up to 64 keys copied straight from global memory
+// into double-buffered row-major LDS tiles by the memory unit (V^T is read
+// from the V tile by LDS transpose reads).  Per tile and wave:
 //   S^T = K Q^T * scale * log2(e)          (MFMA, fp32 accumulate)
 //   mask only on PARTIAL tiles (diagonal chunk pair: key offset <= query
 //   offset); keys past the ragged tile end are masked on every tile
@@ -28,6 +30,9 @@ namespace zz {
 namespace {
 
 constexpr int kWaves = 4;
+// s_waitcnt immediate that waits for vmcnt = 0 only (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others at their maximum).
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per LDS tile
@@ -50,16 +55,12 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_FWD_WAVES)))
 fwd_step_kernel(FwdArgs a) {
     using M = Mfma<T, D>;
-    // Waves 0-1 stage V (its transposed copy), waves 2-3 stage K (row-major).
-    using Stage = TileStageT<T, D, kBN, kThreads / 2>;
-    constexpr int LD = M::LD;
-    constexpr int LDT = Stage::LDT;
-    constexpr int SLOTS = Stage::NQ;
+    using DmaKV = Dma<kBN, M::W, kWaves>;
     constexpr int NB = D / 32;   // 32-wide head-dim blocks of O^T
-    // Double-buffered: K row-major (A operand of S^T = K Q^T), V transposed
-    // (A operand of O^T = V^T P^T).  One barrier per tile.
-    __shared__ __attribute__((aligned(16))) T Ks[2][kBN * LD];
-    __shared__ __attribute__((aligned(16))) T Vt[2][D * LDT];
+    // Double-buffered row-major K (A operand of S^T = K Q^T) and V (read
+    // transposed as the A operand of O^T = V^T P^T).  One barrier per tile.
+    __shared__ __attribute__((aligned(16))) T Ks[2][kBN * D];
+    __shared__ __attribute__((aligned(16))) T Vs[2][kBN * D];
 
     const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -103,37 +104,28 @@ fwd_step_kernel(FwdArgs a) {
     float m = -INFINITY, lsum = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
-    Stage st;
-    st.init(a.hkv);
-    const bool stage_v = wave < 2;               // wave-uniform
-    const int st_t = tid % (kThreads / 2);
-    auto fetch = [&](int t) {
+    auto copy_tile = [&](int t, int buf) {
         const TileRec tn = load_const(a.tiles, t);
-        st.load(tile_base<T, D>(stage_v ? v : k, kv_row0 + tn.b0, a.hkv, kvh), tn.b1 - tn.b0, st_t);
+        const int nk = tn.b1 - tn.b0;
+        const uint32_t stride = (uint32_t)(a.hkv * D * sizeof(T));
+        DmaKV::issue_rows(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), stride, nk, Ks[buf], wave, lane);
+        DmaKV::issue_rows(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), stride, nk, Vs[buf], wave, lane);
     };
-    auto stash = [&](int buf) {
-        if (stage_v) st.store(Vt[buf], st_t);
-        else st.store_rows(Ks[buf], st_t);
-    };
-    fetch(it.tbeg);
-    stash(0);
-    fetch(min(it.tbeg + 1, it.tend - 1));
+    copy_tile(it.tbeg, 0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     for (int t = it.tbeg; t < it.tend; ++t) {
         const int buf = (t - it.tbeg) & 1;
         const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
-        // Tile t+1, loaded during the previous tile, goes to the other buffer
-        // (its last reader finished before the barrier that ended the
-        // previous tile), then the loads of tile t+2 are issued; both overlap
-        // this tile's compute.  They run on every iteration (past the end they
-        // re-read the last tile into the unused buffer), so every load is
-        // consumed on every path and no wait is needed before a load.
-        stash(buf ^ 1);
-        fetch(min(t + 2, it.tend - 1));
+        // Tile t+1 is copied into the other buffer (its last reader finished
+        // before the barrier that ended the previous tile) while this tile is
+        // computed; past the end the copy re-reads the last tile into the
+        // unused buffer.
+        copy_tile(min(t + 1, it.tend - 1), buf ^ 1);
         if (wave_on) {
             const T *ks = Ks[buf];
-            const T *vt = Vt[buf];
+            const T *vs = Vs[buf];
             f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -176,9 +168,10 @@ fwd_step_kernel(FwdArgs a) {
                     ps += p;
                 }
             lsum += ps;
-            M::template gemm_t_c<LDT, SLOTS>(acc, vt, 0, s[0], lane);
-            M::template gemm_t_c<LDT, SLOTS>(acc, vt, 32, s[1], lane);
+            M::gemm_t_c(acc, vs, 0, s[0], lane);
+            M::gemm_t_c(acc, vs, 32, s[1], lane);
         }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile t+1 have landed
         __syncthreads();
     }
     if (!row_ok) return;

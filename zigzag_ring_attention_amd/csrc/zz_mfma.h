@@ -10,8 +10,21 @@
 // per lane column: the softmax row statistics of a query live in one lane
 // pair (l, l^32).  P^T in C layout becomes the B operand of O^T = V^T P^T
 // after one exchange between the lane halves (order_for_b), which puts the
-// keys of a lane half in natural order; the A operand (V^T) is read from a
-// transposed LDS copy whose rows hold the keys in natural order.
+// keys of a lane half in natural order.  Operands that run down the columns
+// of a row-major tile (V^T, Q^T, dO^T, K^T) are read from that same tile with
+// the LDS transpose read ds_read_b64_tr_b16 (layout below), so every tile is
+// staged once, row-major.
+//
+//  ds_read_b64_tr_b16 (checked on the device; independent of the addresses):
+//    in each group of 16 lanes, lane i receives element i%4 of the 8-byte
+//    chunks fetched by lanes i/4 + 4j of its group, j = 0..3, as its
+//    elements j.  So if lane c + 4j of a group fetches 4 columns starting at
+//    4c of row j, lane i ends up with column i of rows 0..3.
+//
+// LDS tiles are unpadded and XOR-swizzled in 16-byte slots (Swz), and are
+// filled by the memory unit straight from global memory (global_load_lds, 16
+// bytes per lane): a wave instruction writes 1 KB of contiguous LDS, so the
+// swizzle is applied by choosing which global slot each lane fetches.
 #pragma once
 
 #include "zz_device.h"
@@ -64,22 +77,74 @@ __device__ __forceinline__ float swap_halves(float x, int lane) {
     return __uint_as_float(lane < 32 ? r[1] : r[0]);
 }
 
-template <typename T, int D> struct Mfma;
-
-// bf16 operands, v_mfma_f32_32x32x16_bf16.
-// Row-major LDS tiles: 16 bytes of padding per row, so the 16 rows read by
-// 16 lanes (one row per lane, same column) start on 16 different bank
-// groups.
-template <typename T, int D> struct RowLayout {
-    static constexpr int EPV = 16 / sizeof(T);
-    static constexpr int LD = D + EPV;   // row stride (elements)
-    static __device__ __forceinline__ int at(int r, int e) { return r * LD + e; }
+// Tile rows of W 16-byte slots, unpadded: logical slot s of row r sits at
+// slot r*W + (s ^ key(r)).  The key is chosen so that both read patterns of
+// the kernels touch each 16-byte group of a 256-byte bank window once:
+//  - row reads: 16 consecutive rows (aligned to 16) at one logical slot;
+//  - transpose reads: 4 consecutive rows (aligned to 4) x 4 consecutive
+//    slots (aligned to 4).
+// For W <= 16 a row covers W groups of the window and 16/W rows share one
+// window; key = 4 * ((r / (16/W)) % (W/4)) + (r/4) % 4 puts the rows of an
+// aligned 4-row set on distinct 4-slot quarters and 16 aligned rows on
+// distinct groups.  Wider rows (fp32 with D = 128) use key = r % 16.
+template <int W> struct Swz {
+    static_assert(W == 4 || W == 8 || W == 16 || W == 32, "row width in 16-byte slots");
+    static __device__ __forceinline__ constexpr int key(int r) {
+        return W > 16 ? r % 16 : 4 * ((r / (16 / W)) % (W / 4)) + (r / 4) % 4;
+    }
+    static __device__ __forceinline__ constexpr int slot(int r, int s) { return r * W + (s ^ key(r)); }
 };
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One 1 KB block of a global -> LDS copy: lane l's 16 bytes at `src` land at
+// LDS byte lds + 16*l.  Written as inline asm so the compiler's counter
+// bookkeeping does not see an LDS write in flight (it cannot tell the two
+// buffers apart and would wait for the copy before every LDS read of the
+// other buffer); the issuing wave orders it with s_waitcnt vmcnt(0) and a
+// barrier before any wave reads the block.
+// M0 is named as clobbered; the kernels give the compiler no other use of it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_block(const char *src, void *lds) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Global -> LDS copy of a tile of ROWS rows x W 16-byte slots into the Swz<W>
+// image, by NW waves (wave w issues instructions w, w+NW, ...; each moves
+// 64 slots = 1 KB).  Row r of the tile is global row min(r, nrows-1) at
+// gbase + row * gstride bytes (rows past a ragged tile re-read its last row;
+// the kernels give them zero weight).
+// Completion: s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
+template <int ROWS, int W, int NW> struct Dma {
+    static constexpr int INSTR = ROWS * W / 64;
+    static_assert((ROWS * W) % 64 == 0, "a tile is a whole number of 1 KB blocks");
+    static __device__ __forceinline__ void issue_rows(const char *gbase, uint32_t gstride, int nrows, void *lds,
+                                                      int wave, int lane) {
+        const int w = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+        for (int k0 = 0; k0 < INSTR; k0 += NW) {
+            const int k = k0 + w;
+            if (INSTR % NW != 0 && k >= INSTR) break;
+            const int pu = k * 64 + lane;
+            const int r = pu / W;
+            const int sl = (pu % W) ^ Swz<W>::key(r);
+            const uint32_t rr = (uint32_t)min(r, nrows - 1);
+            dma_block(gbase + rr * gstride + (uint32_t)(sl * 16), (char *)lds + k * 1024);
+        }
+    }
+};
+
+template <typename T, int D> struct Mfma;
+
+// bf16 operands, v_mfma_f32_32x32x16_bf16.  Row-major LDS tiles hold D
+// elements (W = D/8 slots) per row in the Swz layout.
 template <int D> struct Mfma<bf16, D> {
     static constexpr int KS = D / 16;   // contraction steps over the head dim
-    using RL = RowLayout<bf16, D>;
-    static constexpr int LD = RL::LD;   // row-major LDS row stride (elements)
+    static constexpr int W = D / 8;     // slots per row-major tile row
     typedef bf16x8 Op;
 
     // Row-major operand of one lane: 8 consecutive values at column 16*ks + 8*hh.
@@ -93,15 +158,17 @@ template <int D> struct Mfma<bf16, D> {
 #pragma unroll
             for (int e = 0; e < 8; ++e) op[ks][e] = bf16(0.0f);
     }
+    // A operand of step ks from row `row` of a row-major tile.
+    static __device__ __forceinline__ bf16x8 row_frag(const bf16 *tile, int row, int ks, int hh) {
+        return *reinterpret_cast<const bf16x8 *>(tile + 8 * Swz<W>::slot(row, 2 * ks + hh));
+    }
     // acc += A x B(op), A = row `row` of a row-major LDS tile (one row per
     // lane: row = r0 + l%32), contraction over D.
     static __device__ __forceinline__ void gemm_rows_lds(f32x16 &acc, const bf16 *tile, int row, const Op (&op)[KS],
                                                          int hh) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row, 16 * ks + 8 * hh));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, op[ks], acc, 0, 0, 0);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(tile, row, ks, hh), op[ks], acc, 0, 0, 0);
     }
     // Two chains over the same operand op: acc0 += rows row0.. x op and
     // acc1 += rows row1.. x op.  The LDS operands of a step are read one step
@@ -109,14 +176,13 @@ template <int D> struct Mfma<bf16, D> {
     // accumulator dependency stalls the matrix unit.
     static __device__ __forceinline__ void gemm_rows_lds2(f32x16 &acc0, f32x16 &acc1, const bf16 *tile, int row0,
                                                           int row1, const Op (&op)[KS], int hh) {
-        bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row0, 8 * hh));
-        bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row1, 8 * hh));
+        bf16x8 a0 = row_frag(tile, row0, 0, hh), a1 = row_frag(tile, row1, 0, hh);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             bf16x8 n0 = a0, n1 = a1;
             if (ks + 1 < KS) {
-                n0 = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row0, 16 * (ks + 1) + 8 * hh));
-                n1 = *reinterpret_cast<const bf16x8 *>(tile + RL::at(row1, 16 * (ks + 1) + 8 * hh));
+                n0 = row_frag(tile, row0, ks + 1, hh);
+                n1 = row_frag(tile, row1, ks + 1, hh);
             }
             acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, op[ks], acc0, 0, 0, 0);
             acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, op[ks], acc1, 0, 0, 0);
@@ -128,14 +194,13 @@ template <int D> struct Mfma<bf16, D> {
     static __device__ __forceinline__ void gemm_rows_lds_pair(f32x16 &acc0, const bf16 *tile0, const Op (&op0)[KS],
                                                               f32x16 &acc1, const bf16 *tile1, const Op (&op1)[KS],
                                                               int row, int hh) {
-        bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(tile0 + RL::at(row, 8 * hh));
-        bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(tile1 + RL::at(row, 8 * hh));
+        bf16x8 a0 = row_frag(tile0, row, 0, hh), a1 = row_frag(tile1, row, 0, hh);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             bf16x8 n0 = a0, n1 = a1;
             if (ks + 1 < KS) {
-                n0 = *reinterpret_cast<const bf16x8 *>(tile0 + RL::at(row, 16 * (ks + 1) + 8 * hh));
-                n1 = *reinterpret_cast<const bf16x8 *>(tile1 + RL::at(row, 16 * (ks + 1) + 8 * hh));
+                n0 = row_frag(tile0, row, ks + 1, hh);
+                n1 = row_frag(tile1, row, ks + 1, hh);
             }
             acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, op0[ks], acc0, 0, 0, 0);
             acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, op1[ks], acc1, 0, 0, 0);
@@ -143,26 +208,33 @@ template <int D> struct Mfma<bf16, D> {
             a1 = n1;
         }
     }
-    // acc[cb] += X^T * P for a tile X stored transposed in LDS (row = column
-    // of X, LDT elements per row, X rows in natural order): X rows r0..r0+31
-    // against a 32 x 32 block P in C layout.  16-byte reads, two MFMAs per 32
-    // contraction rows and 32 columns; all LDS operands of the block are read
-    // before the first MFMA, so only the first read's latency shows.
-    // The transposed tile is a TileStageT copy: SLOTS 16-byte slots per row,
-    // swizzled by TileStageT::tpos.
-    template <int LDT, int SLOTS>
-    static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const bf16 *tileT, int r0,
+    // A operand of X^T for the 16 contraction rows r0.. (r0 % 4 == 0) and
+    // the 32 columns 32*cb.. of a row-major Swz<W> tile X: lane l gets
+    // X[r0 + 8*hh + e][32*cb + l%32], e = 0..7, from two transpose reads
+    // (e = 0..3 and 4..7).  For a read, lane c + 4j of group g fetches 4
+    // columns from 32*cb + 16*(g%2) + 4c of row r0 + 8*(g/2) + j (+4).
+    static __device__ __forceinline__ bf16x8 col_frag(const bf16 *tile, int r0, int cb, int lane) {
+        const int g = lane >> 4, i = lane & 15;
+        const int row = r0 + 8 * (g >> 1) + (i >> 2);
+        const int col = 32 * cb + 16 * (g & 1) + 4 * (i & 3);
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(tile + 8 * Swz<W>::slot(row, col / 8) + col % 8));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4 *)(tile + 8 * Swz<W>::slot(row + 4, col / 8) + col % 8));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+    // acc[cb] += X^T * P for rows r0..r0+31 of a row-major Swz<W> tile X
+    // against a 32 x 32 block P in C layout (columns of X as the MFMA rows).
+    // All LDS operands of the block are read before the first MFMA, so only
+    // the first read's latency shows.
+    static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const bf16 *tile, int r0,
                                                     const f32x16 &p, int lane) {
-        const int hh = lane >> 5;
         bf16x8 a[2][D / 32];
 #pragma unroll
         for (int half = 0; half < 2; ++half)
 #pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const int row = 32 * cb + (lane & 31);
-                const int slot = ((r0 + 16 * half + 8 * hh) / 8) ^ ((row >> 4) & (SLOTS - 1));
-                a[half][cb] = *reinterpret_cast<const bf16x8 *>(tileT + row * LDT + 8 * slot);
-            }
+            for (int cb = 0; cb < D / 32; ++cb) a[half][cb] = col_frag(tile, r0 + 16 * half, cb, lane);
         f32x16 pb = p;
         order_for_b(pb);
 #pragma unroll
@@ -177,11 +249,10 @@ template <int D> struct Mfma<bf16, D> {
     }
 };
 
-// fp32 operands, v_mfma_f32_32x32x2_f32.
+// fp32 operands, v_mfma_f32_32x32x2_f32 (W = D/4 slots per row-major row).
 template <int D> struct Mfma<float, D> {
     static constexpr int KS = D / 2;
-    using RL = RowLayout<float, D>;
-    static constexpr int LD = RL::LD;
+    static constexpr int W = D / 4;
     typedef float Op;
 
     static __device__ __forceinline__ void load_row_op(Op (&op)[KS], const float *row, int hh) {
@@ -192,11 +263,16 @@ template <int D> struct Mfma<float, D> {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) op[ks] = 0.0f;
     }
+    // Element (row, col) of a Swz<WS> tile of 4-element slots.
+    template <int WS>
+    static __device__ __forceinline__ float at(const float *tile, int row, int col) {
+        return tile[4 * Swz<WS>::slot(row, col / 4) + col % 4];
+    }
     static __device__ __forceinline__ void gemm_rows_lds(f32x16 &acc, const float *tile, int row, const Op (&op)[KS],
                                                          int hh) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(tile[RL::at(row, 2 * ks + hh)], op[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(at<W>(tile, row, 2 * ks + hh), op[ks], acc, 0, 0, 0);
     }
     static __device__ __forceinline__ void gemm_rows_lds2(f32x16 &acc0, f32x16 &acc1, const float *tile, int row0,
                                                           int row1, const Op (&op)[KS], int hh) {
@@ -209,19 +285,19 @@ template <int D> struct Mfma<float, D> {
         gemm_rows_lds(acc0, tile0, row, op0, hh);
         gemm_rows_lds(acc1, tile1, row, op1, hh);
     }
-    template <int LDT, int SLOTS>
-    static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const float *tileT, int r0,
+    // acc[cb] += X^T * P for rows r0..r0+31 of a row-major tile X against a
+    // 32 x 32 block P in C layout: one contraction row per MFMA, the lanes
+    // of a half reading 32 consecutive columns of it.
+    static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const float *tile, int r0,
                                                     const f32x16 &p, int lane) {
         const int hh = lane >> 5;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int pos = r0 + c_row(i, hh);
 #pragma unroll
-            for (int cb = 0; cb < D / 32; ++cb) {
-                const int row = 32 * cb + (lane & 31);
-                const int at = (((pos / 4) ^ ((row >> 4) & (SLOTS - 1))) * 4) + pos % 4;
-                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(tileT[row * LDT + at], p[i], acc[cb], 0, 0, 0);
-            }
+            for (int cb = 0; cb < D / 32; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(at<W>(tile, pos, 32 * cb + (lane & 31)), p[i],
+                                                                acc[cb], 0, 0, 0);
         }
     }
 };
@@ -233,137 +309,5 @@ template <typename T, int D>
 __device__ __forceinline__ const char *tile_base(const T *g, int64_t row0, int heads, int h) {
     return reinterpret_cast<const char *>(g + (row0 * heads + h) * D);
 }
-
-// A tile of ROWS rows x D columns of a [*, H, D] tensor (one head), staged
-// global -> registers -> LDS by NT threads.  Issuing the global loads for the
-// next tile before computing on the current one hides their latency.
-// Rows past nrows (a ragged tile) re-read row nrows-1, so every load stays
-// inside the tile's chunk and the code has no branch; the kernels give those
-// rows zero weight (masked scores, or an infinite LSE).
-template <typename T, int D, int ROWS, int NT> struct TileStage {
-    static constexpr int EPV = 16 / sizeof(T);   // elements per 16-byte chunk
-    static constexpr int CPR = D / EPV;          // chunks per row
-    static constexpr int N = ROWS * CPR / NT;    // chunks per thread
-    static_assert(N >= 1 && (ROWS * CPR) % NT == 0, "tile must split evenly over the threads");
-    static constexpr int LD = RowLayout<T, D>::LD;
-    i32x4 r[N];
-    uint32_t rstride;   // bytes between consecutive rows (wave-uniform)
-
-    // Chunk c = tid + i*NT is row c / CPR, elements (c % CPR)*EPV.. of it.
-    __device__ __forceinline__ void init(int heads, int tid) { rstride = (uint32_t)(heads * D * sizeof(T)); }
-    __device__ __forceinline__ void load(const char *base, int nrows, int tid) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int c = tid + i * NT;
-            const uint32_t rr = (uint32_t)min(c / CPR, nrows - 1);
-            r[i] = *reinterpret_cast<const i32x4 *>(base + rr * rstride + (uint32_t)((c % CPR) * 16));
-        }
-    }
-    __device__ __forceinline__ void store(T *lds, int tid) const {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int c = tid + i * NT, e = (c % CPR) * EPV;
-            *reinterpret_cast<i32x4 *>(lds + (c / CPR) * LD + e) = r[i];
-        }
-    }
-};
-
-// A tile of ROWS rows x D columns of a [*, H, D] tensor (one head), staged
-// global -> registers -> LDS as a row-major copy (RowLayout) and a transposed
-// copy: LDS row c holds column c of the tile, the tile rows in natural order
-// in 16-byte groups whose slots are XOR-swizzled by the row (tpos), with
-// LDT = ROWS + 16 bytes of padding per row.  A unit is RU = 16/sizeof(T)
-// consecutive rows x one 16-byte column group; its RU x RU block is
-// transposed in registers, so both copies are written with 16-byte stores
-// (narrower LDS stores run far below the 16-byte ones).  Units are dealt to
-// the NT staging threads column-group first, so each global load of a wave
-// reads whole rows and the row-major stores of 16 lanes fill consecutive
-// 16-byte slots; the swizzle does the same for the transposed stores, whose
-// 16 lanes would otherwise land on two bank groups.  Rows past nrows re-read
-// row nrows-1 (see TileStage).
-template <typename T, int D, int ROWS, int NT> struct TileStageT {
-    static constexpr int EPV = 16 / sizeof(T);   // elements per 16-byte chunk
-    static constexpr int RU = EPV;               // rows per unit
-    static constexpr int CPR = D / EPV;          // 16-byte column groups
-    static constexpr int NQ = ROWS / RU;         // row units
-    static constexpr int UNITS = NQ * CPR;
-    static constexpr int N = (UNITS + NT - 1) / NT;
-    static constexpr int LDT = ROWS + EPV;       // transposed row stride (elements)
-    static_assert(ROWS % RU == 0, "rows must split into units");
-    static_assert((NQ & (NQ - 1)) == 0, "row units must be a power of two");
-    i32x4 r[N][RU];
-    uint32_t rstride;   // bytes between consecutive rows (wave-uniform)
-
-    // unit -> (row unit m, column group cg)
-    static __device__ __forceinline__ void unit(int u, int &m, int &cg) {
-        m = u / CPR;
-        cg = u % CPR;
-    }
-    // Element offset of tile row `pos` inside transposed LDS row `row`: the
-    // 16-byte slot is XOR-ed with bits 4.. of the row, so 16 consecutive
-    // rows read the same slot conflict-free (odd row stride in slots) and the
-    // 16 rows cg*EPV + c written by 16 lanes spread over all slots.
-    static __device__ __forceinline__ constexpr int tpos(int row, int pos) {
-        return (((pos / EPV) ^ ((row >> 4) & (NQ - 1))) * EPV) + pos % EPV;
-    }
-    __device__ __forceinline__ void init(int heads) { rstride = (uint32_t)(heads * D * sizeof(T)); }
-    // t: this thread's index among the NT staging threads.
-    __device__ __forceinline__ void load(const char *base, int nrows, int t) {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int u = t + i * NT;
-            if (UNITS % NT != 0 && u >= UNITS) continue;
-            int m, cg;
-            unit(u, m, cg);
-#pragma unroll
-            for (int j = 0; j < RU; ++j) {
-                const uint32_t rr = (uint32_t)min(RU * m + j, nrows - 1);
-                r[i][j] = *reinterpret_cast<const i32x4 *>(base + rr * rstride + (uint32_t)(cg * 16));
-            }
-        }
-    }
-    // Row-major copy (the layout of RowLayout).
-    __device__ __forceinline__ void store_rows(T *lds, int t) const {
-        using RL = RowLayout<T, D>;
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int u = t + i * NT;
-            if (UNITS % NT != 0 && u >= UNITS) continue;
-            int m, cg;
-            unit(u, m, cg);
-#pragma unroll
-            for (int j = 0; j < RU; ++j) *reinterpret_cast<i32x4 *>(lds + (RU * m + j) * RL::LD + cg * EPV) = r[i][j];
-        }
-    }
-    // Element c (0..EPV-1) of row j of unit i, as the low bits of a word.
-    __device__ __forceinline__ uint32_t half_of(int i, int j, int c) const {
-        const uint32_t w = (uint32_t)r[i][j][c / 2];
-        return (c & 1) ? (w >> 16) : (w & 0xffffu);
-    }
-    // Transposed copy: column c of the unit's column group is LDS row
-    // cg*EPV + c, the unit's RU rows at positions RU*m .. RU*m+RU-1.
-    __device__ __forceinline__ void store(T *ldsT, int t) const {
-#pragma unroll
-        for (int i = 0; i < N; ++i) {
-            const int u = t + i * NT;
-            if (UNITS % NT != 0 && u >= UNITS) continue;
-            int m, cg;
-            unit(u, m, cg);
-#pragma unroll
-            for (int c = 0; c < EPV; ++c) {
-                u32x4 col;
-                if constexpr (sizeof(T) == 2) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) col[k] = half_of(i, 2 * k, c) | (half_of(i, 2 * k + 1, c) << 16);
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) col[k] = (uint32_t)r[i][k][c];
-                }
-                const int row = cg * EPV + c;
-                *reinterpret_cast<u32x4 *>(ldsT + row * LDT + tpos(row, RU * m)) = col;
-            }
-        }
-    }
-};
 
 }  // namespace zz

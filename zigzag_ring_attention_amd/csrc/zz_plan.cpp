@@ -198,7 +198,8 @@ zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, in
     PassTables &fw = p->pass[ZZ_PASS_FWD];
     fw.bm = bm; fw.bn = bn; fw.key_major = false; fw.keep_empty = true;
     PassTables &dq = p->pass[ZZ_PASS_BWD_DQ];
-    dq.bm = 128; dq.bn = 64; dq.key_major = false; dq.keep_empty = false;
+    // dQ: 256 query rows per item; fp32 key tiles halved for D >= 64 (LDS).
+    dq.bm = 256; dq.bn = (dt == ZZ_F32 && d >= 64) ? 32 : 64; dq.key_major = false; dq.keep_empty = false;
     PassTables &dkv = p->pass[ZZ_PASS_BWD_DKV];
     // fp32 query tiles of 64 or 128 columns are halved so the double-buffered
     // LDS stage of the dK/dV kernel fits.
