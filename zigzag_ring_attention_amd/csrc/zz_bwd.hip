@@ -138,7 +138,8 @@ bwd_dkv_kernel(BwdArgs a) {
     // registers of the first kQT threads (rows past the tile get LSE = +inf,
     // so their P and dS are exactly 0).
     float lse_r = 0.0f, dlt_r = 0.0f;
-    auto copy_tile = [&](int u, int buf) {
+    const DmaRows dma((uint32_t)(a.hq * D * sizeof(T)), wave, lane);
+    auto copy_tile = [&](int u, T *qs, T *ds) __attribute__((always_inline)) {
         const int h = kvh * G + u / ntile;
         const TileRec tn = load_const(a.tiles, it.tbeg + u % ntile);
         const int nq = tn.b1 - tn.b0;
@@ -147,27 +148,24 @@ bwd_dkv_kernel(BwdArgs a) {
             lse_r = ok ? a.lse[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : INFINITY;   // scaled when stored
             dlt_r = ok ? a.delta[(int64_t)h * a.T + qrow0 + tn.b0 + tid] : 0.0f;
         }
-        const uint32_t rstride = (uint32_t)(a.hq * D * sizeof(T));
-        DmaRows::issue_rows(tile_base<T, D>(q, qrow0 + tn.b0, a.hq, h), rstride, nq, Qs[buf], wave, lane);
-        DmaRows::issue_rows(tile_base<T, D>(dout, qrow0 + tn.b0, a.hq, h), rstride, nq, Ds[buf], wave, lane);
+        dma.issue(tile_base<T, D>(q, qrow0 + tn.b0, a.hq, h), nq, qs);
+        dma.issue(tile_base<T, D>(dout, qrow0 + tn.b0, a.hq, h), nq, ds);
     };
-    auto store_stats = [&](int buf) {
+    auto store_stats = [&](float *lse_c, float *dlt_c) __attribute__((always_inline)) {
         if (tid < kQT) {
-            lse_s[buf][tid] = lse_r * kLog2e;
-            dlt_s[buf][tid] = dlt_r;
+            lse_c[tid] = lse_r * kLog2e;
+            dlt_c[tid] = dlt_r;
         }
     };
-    copy_tile(0, 0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the key-side operand and tile 0 have landed
-    store_stats(0);
-    __syncthreads();
-    for (int u = 0; u < nwork; ++u) {
-        const int buf = u & 1;
+    // One tile: the copy of tile u+1 into the other buffer (its last readers
+    // finished before the barrier that ended the previous tile) is issued
+    // first and overlaps this tile's work; past the end it re-reads the last
+    // tile.  Called with constant buffers (the loop below is unrolled by
+    // two), so every LDS address is a lane offset plus an immediate.
+    auto tile_step = [&](int u, const T *qs, const T *ds, const float *lse_c, const float *dlt_c, T *qs_next,
+                         T *ds_next, float *lse_next, float *dlt_next) __attribute__((always_inline)) {
         const TileRec tr = load_const(a.tiles, it.tbeg + u % ntile);
-        // Tile u+1 is copied into the other buffer (its last readers finished
-        // before the barrier that ended the previous tile) while this tile is
-        // computed; past the end the copy re-reads the last tile.
-        copy_tile(min(u + 1, nwork - 1), buf ^ 1);
+        copy_tile(min(u + 1, nwork - 1), qs_next, ds_next);
         f32x16 x[NQB];   // wave A: P; wave B: dP
         if (pair_on) {
 #pragma unroll
@@ -179,12 +177,12 @@ bwd_dkv_kernel(BwdArgs a) {
             // wave B on the same SIMD.
             if (role_a) __builtin_amdgcn_s_setprio(1);
             if constexpr (NQB == 2)
-                M::gemm_rows_lds2(x[0], x[1], role_a ? Qs[buf] : Ds[buf], lane & 31, 32 + (lane & 31), op, hh);
+                M::gemm_rows_lds2(x[0], x[1], role_a ? qs : ds, lane & 31, 32 + (lane & 31), op, hh);
             else
-                M::gemm_rows_lds(x[0], role_a ? Qs[buf] : Ds[buf], lane & 31, op, hh);
+                M::gemm_rows_lds(x[0], role_a ? qs : ds, lane & 31, op, hh);
             if (role_a) {
                 __builtin_amdgcn_s_setprio(0);
-                const float *ls = lse_s[buf];
+                const float *ls = lse_c;
                 // Only partial (diagonal) tiles need a mask: query rows past a
                 // ragged tile have P = 0 through their LSE, and the columns of
                 // keys past a ragged item are never written.  Query row qq
@@ -220,9 +218,9 @@ bwd_dkv_kernel(BwdArgs a) {
             if (role_a) {
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb)
-                    M::gemm_t_c(acc, Ds[buf], qb * 32, x[qb], lane);
+                    M::gemm_t_c(acc, ds, qb * 32, x[qb], lane);
             } else {
-                const float *dl = dlt_s[buf];
+                const float *dl = dlt_c;
 #pragma unroll
                 for (int qb = 0; qb < NQB; ++qb) {
                     float4 d4[4];
@@ -241,13 +239,21 @@ bwd_dkv_kernel(BwdArgs a) {
                             x[qb][i] = static_cast<float>(pv[e]) * (x[qb][i] - dv);
                         }
                     }
-                    M::gemm_t_c(acc, Qs[buf], qb * 32, x[qb], lane);
+                    M::gemm_t_c(acc, qs, qb * 32, x[qb], lane);
                 }
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile u+1 have landed
-        store_stats(buf ^ 1);
+        store_stats(lse_next, dlt_next);
         __syncthreads();
+    };
+    copy_tile(0, Qs[0], Ds[0]);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the key-side operand and tile 0 have landed
+    store_stats(lse_s[0], dlt_s[0]);
+    __syncthreads();
+    for (int u = 0; u < nwork; u += 2) {
+        tile_step(u, Qs[0], Ds[0], lse_s[0], dlt_s[0], Qs[1], Ds[1], lse_s[1], dlt_s[1]);
+        if (u + 1 < nwork) tile_step(u + 1, Qs[1], Ds[1], lse_s[1], dlt_s[1], Qs[0], Ds[0], lse_s[0], dlt_s[0]);
     }
     if (!key_ok) return;
     if (role_a) add_row<NB>(a.dv + (krow * a.hkv + kvh) * D, acc, 1.0f, hh, a.accumulate != 0);
@@ -310,31 +316,26 @@ bwd_dq_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
-    auto copy_tile = [&](int t, int buf) {
+    const DmaRows dma((uint32_t)(a.hkv * D * sizeof(T)), wave, lane);
+    auto copy_tile = [&](int t, T *ks, T *vs) __attribute__((always_inline)) {
         const TileRec tn = load_const(a.tiles, t);
         const int nk = tn.b1 - tn.b0;
-        const uint32_t rstride = (uint32_t)(a.hkv * D * sizeof(T));
-        DmaRows::issue_rows(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), rstride, nk, Ks[buf], wave, lane);
-        DmaRows::issue_rows(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), rstride, nk, Vs[buf], wave, lane);
+        dma.issue(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), nk, ks);
+        dma.issue(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), nk, vs);
     };
-    copy_tile(it.tbeg, 0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the query-side operands and tile 0 have landed
-    __syncthreads();
-    for (int t = it.tbeg; t < it.tend; ++t) {
-        const int buf = (t - it.tbeg) & 1;
+    // One tile, as in the forward step: the copy of tile t+1 overlaps this
+    // tile's work; constant buffers (loop unrolled by two).
+    auto tile_step = [&](int t, const T *ks, const T *vs, T *ks_next, T *vs_next) __attribute__((always_inline)) {
         const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
-        // Tile t+1 is copied into the other buffer (its last readers finished
-        // before the barrier that ended the previous tile) while this tile is
-        // computed; past the end the copy re-reads the last tile.
-        copy_tile(min(t + 1, it.tend - 1), buf ^ 1);
+        copy_tile(min(t + 1, it.tend - 1), ks_next, vs_next);
         if (wave_on) {
 #pragma unroll
             for (int kb = 0; kb < kKT / 32; ++kb) {
                 f32x16 s, dp;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
-                M::gemm_rows_lds_pair(s, Ks[buf], qop, dp, Vs[buf], dop, kb * 32 + (lane & 31), hh);
+                M::gemm_rows_lds_pair(s, ks, qop, dp, vs, dop, kb * 32 + (lane & 31), hh);
                 // mask (partial and ragged tiles only): key kk is kept iff kk < nk
                 // and, in a partial tile, kk <= qq + delta; rows of queries past
                 // the item are never written
@@ -346,11 +347,18 @@ bwd_dq_kernel(BwdArgs a) {
                     const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
                     dp[i] = p * (dp[i] - dlt);
                 }
-                M::gemm_t_c(acc, Ks[buf], kb * 32, dp, lane);
+                M::gemm_t_c(acc, ks, kb * 32, dp, lane);
             }
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile t+1 have landed
         __syncthreads();
+    };
+    copy_tile(it.tbeg, Ks[0], Vs[0]);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the query-side operands and tile 0 have landed
+    __syncthreads();
+    for (int t = it.tbeg; t < it.tend; t += 2) {
+        tile_step(t, Ks[0], Vs[0], Ks[1], Vs[1]);
+        if (t + 1 < it.tend) tile_step(t + 1, Ks[1], Vs[1], Ks[0], Vs[0]);
     }
     if (!row_ok) return;
     add_row<NB>(a.dq + (zrow * a.hq + head) * D, acc, a.scale, hh, a.accumulate != 0);

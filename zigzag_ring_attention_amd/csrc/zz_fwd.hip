@@ -104,28 +104,24 @@ fwd_step_kernel(FwdArgs a) {
     float m = -INFINITY, lsum = 0.0f;
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
-    auto copy_tile = [&](int t, int buf) {
+    const DmaKV dma((uint32_t)(a.hkv * D * sizeof(T)), wave, lane);
+    auto copy_tile = [&](int t, T *ks, T *vs) __attribute__((always_inline)) {
         const TileRec tn = load_const(a.tiles, t);
         const int nk = tn.b1 - tn.b0;
-        const uint32_t stride = (uint32_t)(a.hkv * D * sizeof(T));
-        DmaKV::issue_rows(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), stride, nk, Ks[buf], wave, lane);
-        DmaKV::issue_rows(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), stride, nk, Vs[buf], wave, lane);
+        dma.issue(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), nk, ks);
+        dma.issue(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), nk, vs);
     };
-    copy_tile(it.tbeg, 0);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    for (int t = it.tbeg; t < it.tend; ++t) {
-        const int buf = (t - it.tbeg) & 1;
+    // One tile: the copy of tile t+1 into the other buffer (its last readers
+    // finished before the barrier that ended the previous tile) is issued
+    // first and overlaps this tile's work; past the end it re-reads the last
+    // tile into the unused buffer.  Called with constant buffers (the loop
+    // below is unrolled by two), so every LDS address is a lane offset plus
+    // an immediate.
+    auto tile_step = [&](int t, const T *ks, const T *vs, T *ks_next, T *vs_next) __attribute__((always_inline)) {
         const TileRec tr = load_const(a.tiles, t);
         const int nk = tr.b1 - tr.b0;
-        // Tile t+1 is copied into the other buffer (its last reader finished
-        // before the barrier that ended the previous tile) while this tile is
-        // computed; past the end the copy re-reads the last tile into the
-        // unused buffer.
-        copy_tile(min(t + 1, it.tend - 1), buf ^ 1);
+        copy_tile(min(t + 1, it.tend - 1), ks_next, vs_next);
         if (wave_on) {
-            const T *ks = Ks[buf];
-            const T *vs = Vs[buf];
             f32x16 s[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
@@ -173,6 +169,13 @@ fwd_step_kernel(FwdArgs a) {
         }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile t+1 have landed
         __syncthreads();
+    };
+    copy_tile(it.tbeg, Ks[0], Vs[0]);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    for (int t = it.tbeg; t < it.tend; t += 2) {
+        tile_step(t, Ks[0], Vs[0], Ks[1], Vs[1]);
+        if (t + 1 < it.tend) tile_step(t + 1, Ks[1], Vs[1], Ks[0], Vs[0]);
     }
     if (!row_ok) return;
 

@@ -8,12 +8,13 @@
 //
 // Scores are formed transposed (S^T = K Q^T), so the C layout puts one query
 // per lane column: the softmax row statistics of a query live in one lane
-// pair (l, l^32).  P^T in C layout becomes the B operand of O^T = V^T P^T
-// after one exchange between the lane halves (order_for_b), which puts the
-// keys of a lane half in natural order.  Operands that run down the columns
-// of a row-major tile (V^T, Q^T, dO^T, K^T) are read from that same tile with
-// the LDS transpose read ds_read_b64_tr_b16 (layout below), so every tile is
-// staged once, row-major.
+// pair (l, l^32).  P^T in C layout is then directly the B operand of
+// O^T = V^T P^T, with the contraction over the keys taken in the order the
+// C layout holds them; the A operand (V^T) is read in the same order.
+// Operands that run down the columns of a row-major tile (V^T, Q^T, dO^T,
+// K^T) are read from that same tile with the LDS transpose read
+// ds_read_b64_tr_b16 (layout below), so every tile is staged once,
+// row-major.
 //
 //  ds_read_b64_tr_b16 (checked on the device; independent of the addresses):
 //    in each group of 16 lanes, lane i receives element i%4 of the 8-byte
@@ -53,24 +54,6 @@ __device__ __forceinline__ void mask_rows_below(f32x16 &x, int bound_hh) {
         if (c_row0(i) < bound_hh) x[i] = -INFINITY;
 }
 
-// Reorder a 32-row block in C layout into B-operand order: afterwards lane
-// half hh holds rows 16*h + 8*hh + e in register 8*h + e (h = 0, 1; e = 0..7),
-// the contraction order of a 32x32x16 MFMA over natural rows.  In C layout
-// half hh holds rows 16*h + 4*hh + {0..3, 8..11}; one permlane32 swap per
-// register pair (j, j+4) exchanges rows 4..7 of half 0 with rows 8..11 of
-// half 1.
-__device__ __forceinline__ void order_for_b(f32x16 &x) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[8 * h + j]), __float_as_uint(x[8 * h + 4 + j]),
-                                                      false, false);
-            x[8 * h + j] = __uint_as_float(r[0]);       // lanes 0-31 keep, 32-63 get rows 8..11 of half 0
-            x[8 * h + 4 + j] = __uint_as_float(r[1]);   // lanes 0-31 get rows 4..7 of half 1, 32-63 keep
-        }
-}
-
 // Exchange a value with lane l^32.
 __device__ __forceinline__ float swap_halves(float x, int lane) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -97,43 +80,60 @@ template <int W> struct Swz {
 
 typedef __attribute__((address_space(3))) char lds_char;
 
-// One 1 KB block of a global -> LDS copy: lane l's 16 bytes at `src` land at
-// LDS byte lds + 16*l.  Written as inline asm so the compiler's counter
-// bookkeeping does not see an LDS write in flight (it cannot tell the two
-// buffers apart and would wait for the copy before every LDS read of the
-// other buffer); the issuing wave orders it with s_waitcnt vmcnt(0) and a
-// barrier before any wave reads the block.
-// M0 is named as clobbered; the kernels give the compiler no other use of it.
+// One 1 KB block of a global -> LDS copy: lane l's 16 bytes at
+// base + off[l] land at LDS byte lds + 16*l (base wave-uniform, in SGPRs).
+// Written as inline asm so the compiler's counter bookkeeping does not see an
+// LDS write in flight (it cannot tell the two buffers apart and would wait
+// for the copy before every LDS read of the other buffer); the issuing wave
+// orders it with s_waitcnt vmcnt(0) and a barrier before any wave reads the
+// block.  M0 is named as clobbered; the kernels give the compiler no other
+// use of it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma_block(const char *src, void *lds) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_char *)lds);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :: "v"(src), "s"(base) : "memory", "m0");
+__device__ __forceinline__ void dma_block(const char *base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 #pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lds_char *)p; }
 
 // Global -> LDS copy of a tile of ROWS rows x W 16-byte slots into the Swz<W>
 // image, by NW waves (wave w issues instructions w, w+NW, ...; each moves
 // 64 slots = 1 KB).  Row r of the tile is global row min(r, nrows-1) at
-// gbase + row * gstride bytes (rows past a ragged tile re-read its last row;
-// the kernels give them zero weight).
+// base + row * gstride bytes (rows past a ragged tile re-read its last row;
+// the kernels give them zero weight).  A lane's byte offsets for a whole
+// tile are computed once; only ragged tiles recompute them.
 // Completion: s_waitcnt vmcnt(0) in the issuing wave, then a barrier.
 template <int ROWS, int W, int NW> struct Dma {
     static constexpr int INSTR = ROWS * W / 64;
+    static constexpr int PER = (INSTR + NW - 1) / NW;   // instructions per wave
     static_assert((ROWS * W) % 64 == 0, "a tile is a whole number of 1 KB blocks");
-    static __device__ __forceinline__ void issue_rows(const char *gbase, uint32_t gstride, int nrows, void *lds,
-                                                      int wave, int lane) {
-        const int w = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t off[PER];
+    uint32_t gstride;
+    int w, lane;
+
+    __device__ __forceinline__ Dma(uint32_t gstride_, int wave, int lane_) : gstride(gstride_), lane(lane_) {
+        w = __builtin_amdgcn_readfirstlane(wave);
 #pragma unroll
-        for (int k0 = 0; k0 < INSTR; k0 += NW) {
-            const int k = k0 + w;
-            if (INSTR % NW != 0 && k >= INSTR) break;
-            const int pu = k * 64 + lane;
-            const int r = pu / W;
-            const int sl = (pu % W) ^ Swz<W>::key(r);
-            const uint32_t rr = (uint32_t)min(r, nrows - 1);
-            dma_block(gbase + rr * gstride + (uint32_t)(sl * 16), (char *)lds + k * 1024);
+        for (int j = 0; j < PER; ++j) off[j] = offset(j, ROWS);
+    }
+    __device__ __forceinline__ uint32_t offset(int j, int nrows) const {
+        const int pu = (j * NW + w) * 64 + lane;
+        const int r = pu / W;
+        const int sl = (pu % W) ^ Swz<W>::key(r);
+        return (uint32_t)min(r, nrows - 1) * gstride + (uint32_t)(sl * 16);
+    }
+    __device__ __forceinline__ void issue(const char *base, int nrows, const void *lds) const {
+        const uint32_t l0 = lds_addr(lds) + (uint32_t)w * 1024u;
+        if (nrows >= ROWS) {
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                if (INSTR % NW == 0 || j * NW + w < INSTR) dma_block(base, off[j], l0 + j * NW * 1024);
+        } else {
+#pragma unroll
+            for (int j = 0; j < PER; ++j)
+                if (INSTR % NW == 0 || j * NW + w < INSTR) dma_block(base, offset(j, nrows), l0 + j * NW * 1024);
         }
     }
 };
@@ -208,26 +208,30 @@ template <int D> struct Mfma<bf16, D> {
             a1 = n1;
         }
     }
-    // A operand of X^T for the 16 contraction rows r0.. (r0 % 4 == 0) and
-    // the 32 columns 32*cb.. of a row-major Swz<W> tile X: lane l gets
-    // X[r0 + 8*hh + e][32*cb + l%32], e = 0..7, from two transpose reads
-    // (e = 0..3 and 4..7).  For a read, lane c + 4j of group g fetches 4
-    // columns from 32*cb + 16*(g%2) + 4c of row r0 + 8*(g/2) + j (+4).
+    // A operand of X^T for one 32x32x16 step over 16 contraction rows of a
+    // row-major Swz<W> tile X, taken in the order the C layout holds them:
+    // lane l gets X[r0 + 8*(e/4) + 4*hh + e%4][32*cb + l%32], e = 0..7
+    // (r0 % 16 == 0), from two transpose reads (e = 0..3 and 4..7).  For a
+    // read, lane c + 4j of group g fetches 4 columns from
+    // 32*cb + 16*(g%2) + 4c of row r0 + 4*(g/2) + j (+8).
     static __device__ __forceinline__ bf16x8 col_frag(const bf16 *tile, int r0, int cb, int lane) {
         const int g = lane >> 4, i = lane & 15;
-        const int row = r0 + 8 * (g >> 1) + (i >> 2);
+        const int row = r0 + 4 * (g >> 1) + (i >> 2);
         const int col = 32 * cb + 16 * (g & 1) + 4 * (i & 3);
         typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             (lds_s16x4 *)(tile + 8 * Swz<W>::slot(row, col / 8) + col % 8));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4 *)(tile + 8 * Swz<W>::slot(row + 4, col / 8) + col % 8));
+            (lds_s16x4 *)(tile + 8 * Swz<W>::slot(row + 8, col / 8) + col % 8));
         return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
     // acc[cb] += X^T * P for rows r0..r0+31 of a row-major Swz<W> tile X
     // against a 32 x 32 block P in C layout (columns of X as the MFMA rows).
-    // All LDS operands of the block are read before the first MFMA, so only
-    // the first read's latency shows.
+    // The contraction runs over the rows in C-layout order: registers
+    // 8*half .. 8*half+7 of a lane half are its B operand of step `half`
+    // as they stand, and col_frag reads X's rows in the same order.  All LDS
+    // operands of the block are read before the first MFMA, so only the
+    // first read's latency shows.
     static __device__ __forceinline__ void gemm_t_c(f32x16 (&acc)[D / 32], const bf16 *tile, int r0,
                                                     const f32x16 &p, int lane) {
         bf16x8 a[2][D / 32];
@@ -235,13 +239,11 @@ template <int D> struct Mfma<bf16, D> {
         for (int half = 0; half < 2; ++half)
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb) a[half][cb] = col_frag(tile, r0 + 16 * half, cb, lane);
-        f32x16 pb = p;
-        order_for_b(pb);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             bf16x8 b;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) b[e] = to_bf16(pb[8 * half + e]);
+            for (int e = 0; e < 8; ++e) b[e] = to_bf16(p[8 * half + e]);
 #pragma unroll
             for (int cb = 0; cb < D / 32; ++cb)
                 acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[half][cb], b, acc[cb], 0, 0, 0);
