@@ -139,9 +139,9 @@ bwd_dkv_kernel(BwdArgs a) {
     // so their P and dS are exactly 0).
     float lse_r = 0.0f, dlt_r = 0.0f;
     const DmaRows dma((uint32_t)(a.hq * D * sizeof(T)), wave, lane);
-    auto copy_tile = [&](int u, T *qs, T *ds) __attribute__((always_inline)) {
+    TileWindow win(a.tiles, it.tbeg, ntile, lane);
+    auto copy_tile = [&](int u, const TileRec &tn, T *qs, T *ds) __attribute__((always_inline)) {
         const int h = kvh * G + u / ntile;
-        const TileRec tn = load_const(a.tiles, it.tbeg + u % ntile);
         const int nq = tn.b1 - tn.b0;
         if (tid < kQT) {   // issued first: the counter waits below do not cover the copies
             const bool ok = tid < nq;
@@ -157,6 +157,7 @@ bwd_dkv_kernel(BwdArgs a) {
             dlt_c[tid] = dlt_r;
         }
     };
+    TileRec cur = win.get(0);
     // One tile: the copy of tile u+1 into the other buffer (its last readers
     // finished before the barrier that ended the previous tile) is issued
     // first and overlaps this tile's work; past the end it re-reads the last
@@ -164,8 +165,10 @@ bwd_dkv_kernel(BwdArgs a) {
     // two), so every LDS address is a lane offset plus an immediate.
     auto tile_step = [&](int u, const T *qs, const T *ds, const float *lse_c, const float *dlt_c, T *qs_next,
                          T *ds_next, float *lse_next, float *dlt_next) __attribute__((always_inline)) {
-        const TileRec tr = load_const(a.tiles, it.tbeg + u % ntile);
-        copy_tile(min(u + 1, nwork - 1), qs_next, ds_next);
+        const TileRec tr = cur;
+        const int un = min(u + 1, nwork - 1);
+        cur = win.get(un % ntile);
+        copy_tile(un, cur, qs_next, ds_next);
         f32x16 x[NQB];   // wave A: P; wave B: dP
         if (pair_on) {
 #pragma unroll
@@ -247,7 +250,7 @@ bwd_dkv_kernel(BwdArgs a) {
         store_stats(lse_next, dlt_next);
         __syncthreads();
     };
-    copy_tile(0, Qs[0], Ds[0]);
+    copy_tile(0, cur, Qs[0], Ds[0]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the key-side operand and tile 0 have landed
     store_stats(lse_s[0], dlt_s[0]);
     __syncthreads();
@@ -317,18 +320,20 @@ bwd_dq_kernel(BwdArgs a) {
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
     const DmaRows dma((uint32_t)(a.hkv * D * sizeof(T)), wave, lane);
-    auto copy_tile = [&](int t, T *ks, T *vs) __attribute__((always_inline)) {
-        const TileRec tn = load_const(a.tiles, t);
+    TileWindow win(a.tiles, it.tbeg, it.tend - it.tbeg, lane);
+    auto copy_tile = [&](const TileRec &tn, T *ks, T *vs) __attribute__((always_inline)) {
         const int nk = tn.b1 - tn.b0;
         dma.issue(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), nk, ks);
         dma.issue(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), nk, vs);
     };
     // One tile, as in the forward step: the copy of tile t+1 overlaps this
     // tile's work; constant buffers (loop unrolled by two).
+    TileRec cur = win.get(0);
     auto tile_step = [&](int t, const T *ks, const T *vs, T *ks_next, T *vs_next) __attribute__((always_inline)) {
-        const TileRec tr = load_const(a.tiles, t);
+        const TileRec tr = cur;
         const int nk = tr.b1 - tr.b0;
-        copy_tile(min(t + 1, it.tend - 1), ks_next, vs_next);
+        cur = win.get(min(t + 1, it.tend - 1) - it.tbeg);
+        copy_tile(cur, ks_next, vs_next);
         if (wave_on) {
 #pragma unroll
             for (int kb = 0; kb < kKT / 32; ++kb) {
@@ -353,7 +358,7 @@ bwd_dq_kernel(BwdArgs a) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile t+1 have landed
         __syncthreads();
     };
-    copy_tile(it.tbeg, Ks[0], Vs[0]);
+    copy_tile(cur, Ks[0], Vs[0]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the query-side operands and tile 0 have landed
     __syncthreads();
     for (int t = it.tbeg; t < it.tend; t += 2) {

@@ -82,6 +82,34 @@ __device__ __forceinline__ T load_const(const T *p, int64_t i) {
     return out;
 }
 
+// The tile records of one work item (first .. first+count-1), fetched 64 at
+// a time with one vector load per lane (lane l holds record wbase + l) and
+// broadcast with readlane: the tile loops issue no scalar loads, whose
+// latency the shared LDS/scalar counter would otherwise expose.  get() is
+// called with wave-uniform indices; it refetches (rarely) when an index
+// leaves the window.
+struct TileWindow {
+    const TileRec *tiles;
+    int first, count, wbase, lane;
+    i32x4 rec;
+    __device__ __forceinline__ TileWindow(const TileRec *t, int first_, int count_, int lane_)
+        : tiles(t), first(first_), count(count_), wbase(0), lane(lane_) {
+        fetch();
+    }
+    __device__ __forceinline__ void fetch() {
+        rec = *reinterpret_cast<const i32x4 *>(tiles + first + min(wbase + lane, count - 1));
+    }
+    __device__ __forceinline__ TileRec get(int j) {
+        if (j < wbase || j >= wbase + 64) {
+            wbase = j & ~63;
+            fetch();
+        }
+        const int l = j - wbase;
+        return TileRec{__builtin_amdgcn_readlane(rec.x, l), __builtin_amdgcn_readlane(rec.y, l),
+                       __builtin_amdgcn_readlane(rec.z, l), __builtin_amdgcn_readlane(rec.w, l)};
+    }
+};
+
 // float -> bf16, round to nearest even (gfx950 converts in hardware).
 __device__ __forceinline__ bf16 to_bf16(float x) { return static_cast<bf16>(x); }
 

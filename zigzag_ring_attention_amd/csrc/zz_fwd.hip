@@ -105,8 +105,8 @@ fwd_step_kernel(FwdArgs a) {
     const int64_t kv_row0 = (int64_t)it.shard * a.n;
 
     const DmaKV dma((uint32_t)(a.hkv * D * sizeof(T)), wave, lane);
-    auto copy_tile = [&](int t, T *ks, T *vs) __attribute__((always_inline)) {
-        const TileRec tn = load_const(a.tiles, t);
+    TileWindow win(a.tiles, it.tbeg, it.tend - it.tbeg, lane);
+    auto copy_tile = [&](const TileRec &tn, T *ks, T *vs) __attribute__((always_inline)) {
         const int nk = tn.b1 - tn.b0;
         dma.issue(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), nk, ks);
         dma.issue(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), nk, vs);
@@ -117,10 +117,12 @@ fwd_step_kernel(FwdArgs a) {
     // tile into the unused buffer.  Called with constant buffers (the loop
     // below is unrolled by two), so every LDS address is a lane offset plus
     // an immediate.
+    TileRec cur = win.get(0);
     auto tile_step = [&](int t, const T *ks, const T *vs, T *ks_next, T *vs_next) __attribute__((always_inline)) {
-        const TileRec tr = load_const(a.tiles, t);
+        const TileRec tr = cur;
         const int nk = tr.b1 - tr.b0;
-        copy_tile(min(t + 1, it.tend - 1), ks_next, vs_next);
+        cur = win.get(min(t + 1, it.tend - 1) - it.tbeg);
+        copy_tile(cur, ks_next, vs_next);
         if (wave_on) {
             f32x16 s[2];
 #pragma unroll
@@ -170,7 +172,7 @@ fwd_step_kernel(FwdArgs a) {
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile t+1 have landed
         __syncthreads();
     };
-    copy_tile(it.tbeg, Ks[0], Vs[0]);
+    copy_tile(cur, Ks[0], Vs[0]);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     for (int t = it.tbeg; t < it.tend; t += 2) {
