@@ -91,9 +91,11 @@ bwd_dkv_kernel(BwdArgs a) {
     constexpr int NW = kDkvThreads / 64;
     using DmaRows = Dma<kQT, M::W, NW>;
     constexpr int NB = D / 32;
-    __shared__ __attribute__((aligned(16))) T Qs[2][kQT * D];
-    __shared__ __attribute__((aligned(16))) T Ds[2][kQT * D];
-    __shared__ __attribute__((aligned(16))) float lse_s[2][kQT], dlt_s[2][kQT];
+    // Three buffers per tile operand: tile k is formed while tile k-1 is
+    // contracted and tile k+1 is copied in.
+    __shared__ __attribute__((aligned(16))) T Qs[3][kQT * D];
+    __shared__ __attribute__((aligned(16))) T Ds[3][kQT * D];
+    __shared__ __attribute__((aligned(16))) float lse_s[3][kQT], dlt_s[3][kQT];
     // P handed from wave A to wave B: fp16 for 16-bit inputs (10-bit mantissa,
     // so the dS that forms dK is close to the one the dQ kernel forms from
     // the same scores), fp32 otherwise.
@@ -101,7 +103,7 @@ bwd_dkv_kernel(BwdArgs a) {
     // its 16 values with 2 (fp16) or 4 (fp32) wide LDS accesses.
     using PexT = typename std::conditional<sizeof(T) == 2, _Float16, float>::type;
     constexpr int PPV = 16 / sizeof(PexT);     // values per 16-byte vector
-    __shared__ __attribute__((aligned(16))) uint4 Pex[4][NQB][16 / PPV][64];
+    __shared__ __attribute__((aligned(16))) uint4 Pex[3][4][NQB][16 / PPV][64];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, hh = lane >> 5;
     const int pair = wave & 3;
@@ -158,105 +160,138 @@ bwd_dkv_kernel(BwdArgs a) {
         }
     };
     TileRec cur = win.get(0);
-    // One tile: the copy of tile u+1 into the other buffer (its last readers
-    // finished before the barrier that ended the previous tile) is issued
-    // first and overlaps this tile's work; past the end it re-reads the last
-    // tile.  Called with constant buffers (the loop below is unrolled by
-    // two), so every LDS address is a lane offset plus an immediate.
-    auto tile_step = [&](int u, const T *qs, const T *ds, const float *lse_c, const float *dlt_c, T *qs_next,
-                         T *ds_next, float *lse_next, float *dlt_next) __attribute__((always_inline)) {
+    // Phase k (k = 0 .. nwork), one barrier each, software-pipelined across
+    // the pair:
+    //   wave A: dV^T += dO(k-1)^T P(k-1)  (P(k-1) still in its registers),
+    //           then S(k), P(k) = exp(S - LSE), P(k) -> LDS;
+    //   wave B: dS(k-1) = P(k-1) (dP(k-1) - delta)  (P from LDS, dP from its
+    //           registers), dK^T += Q(k-1)^T dS(k-1), then dP(k).
+    // Each role finishes the product of tile k-1 before it forms tile k's
+    // block, so it still holds one block of registers, and A's exponentials
+    // overlap B's products on their shared SIMD and vice versa.  Tile k+1 is
+    // copied in at the start of the phase.  Buffers: tile k in c, k-1 in pv,
+    // k+1 in nx (k mod 3, constant after unrolling by three).
+    f32x16 x[NQB];   // wave A: P of the last formed tile; wave B: its dP
+    // Every phase does both halves (a runtime "first/last phase" test here
+    // costs dozens of registers): phase 0 contracts a zero block against
+    // zeroed buffers, which adds exactly 0, and phase nwork forms a block from
+    // a stale (finite) tile that is never used.
+    auto phase = [&](int k, int c, int pv, int nx) __attribute__((always_inline)) {
         const TileRec tr = cur;
-        const int un = min(u + 1, nwork - 1);
-        cur = win.get(un % ntile);
-        copy_tile(un, cur, qs_next, ds_next);
-        f32x16 x[NQB];   // wave A: P; wave B: dP
-        if (pair_on) {
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) x[qb][i] = 0.0f;
-            // Wave A issues its score products at raised priority, so they
-            // finish first and its exponentials overlap the dP products of
-            // wave B on the same SIMD.
-            if (role_a) __builtin_amdgcn_s_setprio(1);
-            if constexpr (NQB == 2)
-                M::gemm_rows_lds2(x[0], x[1], role_a ? qs : ds, lane & 31, 32 + (lane & 31), op, hh);
-            else
-                M::gemm_rows_lds(x[0], role_a ? qs : ds, lane & 31, op, hh);
-            if (role_a) {
-                __builtin_amdgcn_s_setprio(0);
-                const float *ls = lse_c;
-                // Only partial (diagonal) tiles need a mask: query rows past a
-                // ragged tile have P = 0 through their LSE, and the columns of
-                // keys past a ragged item are never written.  Query row qq
-                // sees key kk iff qq >= kk - delta.
-                if (tr.kind != ZZ_TILE_FULL) {
-#pragma unroll
-                    for (int qb = 0; qb < NQB; ++qb) mask_rows_below(x[qb], kk - tr.delta - qb * 32 - 4 * hh);
-                }
-#pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
-                    float4 l4[4];   // LSE of this lane's 16 query rows (4 runs of 4)
-#pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4)
-                        l4[i4] = *reinterpret_cast<const float4 *>(ls + qb * 32 + c_row(4 * i4, hh));
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float lv = i % 4 == 0 ? l4[i / 4].x : i % 4 == 1 ? l4[i / 4].y
-                                       : i % 4 == 2 ? l4[i / 4].z : l4[i / 4].w;
-                        x[qb][i] = __builtin_amdgcn_exp2f(fmaf(x[qb][i], a.scale_log2, -lv));
-                    }
-#pragma unroll
-                    for (int vi = 0; vi < 16 / PPV; ++vi) {
-                        PexT pv[PPV];
-#pragma unroll
-                        for (int e = 0; e < PPV; ++e) pv[e] = static_cast<PexT>(x[qb][vi * PPV + e]);
-                        Pex[pair][qb][vi][lane] = *reinterpret_cast<const uint4 *>(pv);
-                    }
-                }
-            }
+        if (k + 1 < nwork) {
+            cur = win.get((k + 1) % ntile);
+            copy_tile(k + 1, cur, Qs[nx], Ds[nx]);
         }
-        __syncthreads();   // P of every pair is in LDS
         if (pair_on) {
             if (role_a) {
+                {
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb)
-                    M::gemm_t_c(acc, ds, qb * 32, x[qb], lane);
-            } else {
-                const float *dl = dlt_c;
+                    for (int qb = 0; qb < NQB; ++qb) M::gemm_t_c(acc, Ds[pv], qb * 32, x[qb], lane);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keeps the two products' operands apart
+                {
 #pragma unroll
-                for (int qb = 0; qb < NQB; ++qb) {
-                    float4 d4[4];
+                    for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
-                    for (int i4 = 0; i4 < 4; ++i4)
-                        d4[i4] = *reinterpret_cast<const float4 *>(dl + qb * 32 + c_row(4 * i4, hh));
+                        for (int i = 0; i < 16; ++i) x[qb][i] = 0.0f;
+                    if constexpr (NQB == 2)
+                        M::gemm_rows_lds2(x[0], x[1], Qs[c], lane & 31, 32 + (lane & 31), op, hh);
+                    else
+                        M::gemm_rows_lds(x[0], Qs[c], lane & 31, op, hh);
+                    const float *ls = lse_s[c];
+                    // Only partial (diagonal) tiles need a mask: query rows past
+                    // a ragged tile have P = 0 through their LSE, and the
+                    // columns of keys past a ragged item are never written.
+                    // Query row qq sees key kk iff qq >= kk - delta.
+                    if (tr.kind != ZZ_TILE_FULL) {
 #pragma unroll
-                    for (int vi = 0; vi < 16 / PPV; ++vi) {
-                        const uint4 raw = Pex[pair][qb][vi][lane];
-                        const PexT *pv = reinterpret_cast<const PexT *>(&raw);
+                        for (int qb = 0; qb < NQB; ++qb) mask_rows_below(x[qb], kk - tr.delta - qb * 32 - 4 * hh);
+                    }
 #pragma unroll
-                        for (int e = 0; e < PPV; ++e) {
-                            const int i = vi * PPV + e;
-                            const float dv = i % 4 == 0 ? d4[i / 4].x : i % 4 == 1 ? d4[i / 4].y
-                                           : i % 4 == 2 ? d4[i / 4].z : d4[i / 4].w;
-                            x[qb][i] = static_cast<float>(pv[e]) * (x[qb][i] - dv);
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        float4 l4[4];   // LSE of this lane's 16 query rows (4 runs of 4)
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4)
+                            l4[i4] = *reinterpret_cast<const float4 *>(ls + qb * 32 + c_row(4 * i4, hh));
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const float lv = i % 4 == 0 ? l4[i / 4].x : i % 4 == 1 ? l4[i / 4].y
+                                           : i % 4 == 2 ? l4[i / 4].z : l4[i / 4].w;
+                            x[qb][i] = __builtin_amdgcn_exp2f(fmaf(x[qb][i], a.scale_log2, -lv));
+                        }
+#pragma unroll
+                        for (int vi = 0; vi < 16 / PPV; ++vi) {
+                            PexT pv[PPV];
+#pragma unroll
+                            for (int e = 0; e < PPV; ++e) pv[e] = static_cast<PexT>(x[qb][vi * PPV + e]);
+                            Pex[c][pair][qb][vi][lane] = *reinterpret_cast<const uint4 *>(pv);
                         }
                     }
-                    M::gemm_t_c(acc, qs, qb * 32, x[qb], lane);
+                }
+            } else {
+                {
+                    const float *dl = dlt_s[pv];
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb) {
+                        float4 d4[4];
+#pragma unroll
+                        for (int i4 = 0; i4 < 4; ++i4)
+                            d4[i4] = *reinterpret_cast<const float4 *>(dl + qb * 32 + c_row(4 * i4, hh));
+#pragma unroll
+                        for (int vi = 0; vi < 16 / PPV; ++vi) {
+                            const uint4 raw = Pex[pv][pair][qb][vi][lane];
+                            const PexT *pe = reinterpret_cast<const PexT *>(&raw);
+#pragma unroll
+                            for (int e = 0; e < PPV; ++e) {
+                                const int i = vi * PPV + e;
+                                const float dv = i % 4 == 0 ? d4[i / 4].x : i % 4 == 1 ? d4[i / 4].y
+                                               : i % 4 == 2 ? d4[i / 4].z : d4[i / 4].w;
+                                x[qb][i] = static_cast<float>(pe[e]) * (x[qb][i] - dv);
+                            }
+                        }
+                        M::gemm_t_c(acc, Qs[pv], qb * 32, x[qb], lane);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                {
+#pragma unroll
+                    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) x[qb][i] = 0.0f;
+                    if constexpr (NQB == 2)
+                        M::gemm_rows_lds2(x[0], x[1], Ds[c], lane & 31, 32 + (lane & 31), op, hh);
+                    else
+                        M::gemm_rows_lds(x[0], Ds[c], lane & 31, op, hh);
                 }
             }
         }
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile u+1 have landed
-        store_stats(lse_next, dlt_next);
+        if (k + 1 < nwork) {
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile k+1 have landed
+            store_stats(lse_s[nx], dlt_s[nx]);
+        }
         __syncthreads();
     };
     copy_tile(0, cur, Qs[0], Ds[0]);
+#pragma unroll
+    for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[qb][i] = 0.0f;
+    {
+        const uint4 z = {0u, 0u, 0u, 0u};
+        for (int i = tid; i < kQT * D * (int)sizeof(T) / 16; i += kDkvThreads) {
+            reinterpret_cast<uint4 *>(Qs[2])[i] = z;
+            reinterpret_cast<uint4 *>(Ds[2])[i] = z;
+        }
+        for (int i = tid; i < (int)(sizeof(Pex[2]) / 16); i += kDkvThreads) (&Pex[2][0][0][0][0])[i] = z;
+        if (tid < kQT) dlt_s[2][tid] = 0.0f;
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the key-side operand and tile 0 have landed
     store_stats(lse_s[0], dlt_s[0]);
     __syncthreads();
-    for (int u = 0; u < nwork; u += 2) {
-        tile_step(u, Qs[0], Ds[0], lse_s[0], dlt_s[0], Qs[1], Ds[1], lse_s[1], dlt_s[1]);
-        if (u + 1 < nwork) tile_step(u + 1, Qs[1], Ds[1], lse_s[1], dlt_s[1], Qs[0], Ds[0], lse_s[0], dlt_s[0]);
+    for (int k = 0; k <= nwork; k += 3) {
+        phase(k, 0, 2, 1);
+        if (k + 1 <= nwork) phase(k + 1, 1, 0, 2);
+        if (k + 2 <= nwork) phase(k + 2, 2, 1, 0);
     }
     if (!key_ok) return;
     if (role_a) add_row<NB>(a.dv + (krow * a.hkv + kvh) * D, acc, 1.0f, hh, a.accumulate != 0);
