@@ -2,10 +2,13 @@
 
     python -m zigzag_ring_attention_amd.profiling stats  <kernel_stats.csv> <command...>
     python -m zigzag_ring_attention_amd.profiling traffic <fetch.csv> <write.csv> <command...>
+    python -m zigzag_ring_attention_amd.profiling util <counter_collection.csv> <command...>
 
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown
 table.  ``traffic`` turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE``
 counter_collection.csv files into HBM bytes per launch of each libzz kernel.
+``util`` reports the MFMA utilisation and the effective clock of the three
+attention kernels from one counter pass.
 The counters are calibrated against the zigzag permute kernel in the same
 run, a plain row copy whose bytes are known exactly: the first permute of a
 bench step moves T * Hq * d * 2 bytes each way.
@@ -91,6 +94,57 @@ def traffic_text(fetch_csv: str, write_csv: str, command: str, copy_bytes: float
     return "\n".join(lines) + "\n"
 
 
+# MI355X: 8 XCDs of 32 CUs, 4 SIMDs per CU; dense MFMA FLOPs per clock per SIMD.
+XCDS, SIMDS = 8, 256 * 4
+MFMA_FLOP = {"bf16": 32 * 32 * 16 * 2, "f32": 32 * 32 * 2 * 2}   # per 32x32xK instruction
+FLOP_PER_CLK_SIMD = {"bf16": 1024, "f32": 64}
+NOMINAL_GHZ = 2.4
+
+
+def util_markdown(path: str, command: str) -> str:
+    """MFMA utilisation and effective clock per libzz kernel from one
+    `--pmc SQ_INSTS_MFMA SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` pass.
+
+    SQ_INSTS_MFMA counts wave instructions (x FLOP per instruction = the
+    executed matrix work); SQ_VALU_MFMA_BUSY_CYCLES sums the busy cycles of
+    every SIMD's matrix unit; GRBM_GUI_ACTIVE sums the active cycles of the 8
+    XCDs, so GRBM_GUI_ACTIVE / 8 over the dispatch time is the clock."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    dur = collections.defaultdict(dict)
+    dtype = {}
+    for r in csv.DictReader(open(path)):
+        k = short_name(r["Kernel_Name"])
+        if k not in ("fwd_step_kernel", "bwd_dkv_kernel", "bwd_dq_kernel"):
+            continue
+        d = r["Dispatch_Id"]
+        per[k][(d, r["Counter_Name"])] += float(r["Counter_Value"])
+        dur[k][d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        dtype[k] = "bf16" if "DF16b" in r["Kernel_Name"] else "f32"
+    out = ["# MFMA utilisation and clock, rocprofv3 --pmc", "",
+           "Command: `%s`" % command, "",
+           "Per dispatch (mean): executed matrix work = SQ_INSTS_MFMA x FLOP per instruction; "
+           "busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x %d SIMDs); clock = GRBM_GUI_ACTIVE / %d XCDs / time. "
+           "The clock-adjusted peak is %d FLOP/clk/SIMD x %d SIMDs x clock (2.5166 PFLOP/s at %.1f GHz)."
+           % (SIMDS, XCDS, FLOP_PER_CLK_SIMD["bf16"], SIMDS, NOMINAL_GHZ), "",
+           "| kernel | dispatches | ms | executed TFLOP | TFLOP/s | clock GHz | MFMA busy | of nominal peak |",
+           "|---|---|---|---|---|---|---|---|"]
+    for k in ("fwd_step_kernel", "bwd_dkv_kernel", "bwd_dq_kernel"):
+        if k not in dur:
+            continue
+        ds = sorted(dur[k])
+        t = sum(dur[k][d] for d in ds) / len(ds)
+        inst = sum(per[k][(d, "SQ_INSTS_MFMA")] for d in ds) / len(ds)
+        busy = sum(per[k][(d, "SQ_VALU_MFMA_BUSY_CYCLES")] for d in ds) / len(ds)
+        gui = sum(per[k][(d, "GRBM_GUI_ACTIVE")] for d in ds) / len(ds)
+        cyc = gui / XCDS
+        flop = inst * MFMA_FLOP[dtype[k]]
+        nominal = FLOP_PER_CLK_SIMD[dtype[k]] * SIMDS * NOMINAL_GHZ * 1e9
+        out.append("| %s | %d | %.3f | %.3f | %.1f | %.3f | %.3f | %.3f |" % (
+            k, len(ds), t * 1e3, flop / 1e12, flop / t / 1e12, cyc / t / 1e9, busy / (cyc * SIMDS),
+            flop / t / nominal))
+    return "\n".join(out) + "\n"
+
+
 def read_traffic(path: str, kernel: str):
     """HBM bytes per launch of `kernel` from a traffic summary, or None if the
     file is missing or the kernel sources changed since it was taken."""
@@ -107,6 +161,8 @@ def read_traffic(path: str, kernel: str):
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         sys.stdout.write(stats_markdown(sys.argv[2], " ".join(sys.argv[3:])))
+    elif sys.argv[1] == "util":
+        sys.stdout.write(util_markdown(sys.argv[2], " ".join(sys.argv[3:])))
     elif sys.argv[1] == "traffic":
         # copy size of the first permute: Q of the 131072-token, 64-head, d=128 bf16 workload
         import synthetic
