@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-balance", action="store_true")
+    ap.add_argument("--with-backward", action="store_true",
+                    help="also time the backward on a forward-only workload (synthetic dO)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -138,28 +140,29 @@ def main():
     import zigzag_ring_attention_amd as zz
 
     w = synthetic.WORKLOADS[args.workload]
+    backward = w.backward or args.with_backward
     cu = synthetic.cu_seqlens_for(w)
     T, hq, hkv, d, cp = w.total, w.hq, w.hkv, w.d, w.cp
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     log("bench: workload %s T=%d hq=%d hkv=%d d=%d cp=%d dtype=%s backward=%s" %
-        (w.name, T, hq, hkv, d, cp, w.dtype, w.backward))
+        (w.name, T, hq, hkv, d, cp, w.dtype, backward))
     plan = zz.Plan(cu, cp, hq, hkv, d, w.dtype, device=dev)
     useful_pairs, issued_pairs = plan.pair_counts()
     fwd_flops = 4.0 * d * hq * useful_pairs
-    bwd_flops = 2.5 * fwd_flops if w.backward else 0.0
+    bwd_flops = 2.5 * fwd_flops if backward else 0.0
 
-    q, k, v, *rest = synthetic.randn_qkv_device(w.seed, T, hq, hkv, d, w.dtype, dev, with_do=w.backward)
-    do = rest[0] if w.backward else None
+    q, k, v, *rest = synthetic.randn_qkv_device(w.seed, T, hq, hkv, d, w.dtype, dev, with_do=backward)
+    do = rest[0] if backward else None
     tdt = plan.torch_dtype
     f32 = torch.float32
     q_zz, k_zz, v_zz = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    do_zz = torch.empty_like(do) if w.backward else None
+    do_zz = torch.empty_like(do) if backward else None
     o_acc = torch.empty((T, hq, d), dtype=f32, device=dev)
     lse = torch.empty((hq, T), dtype=f32, device=dev)
     o_zz = torch.empty((T, hq, d), dtype=tdt, device=dev)
     o = torch.empty_like(o_zz)
-    if w.backward:
+    if backward:
         delta = torch.empty((hq, T), dtype=f32, device=dev)
         dq_acc = torch.empty((T, hq, d), dtype=f32, device=dev)
         dk_acc = torch.empty((T, hkv, d), dtype=f32, device=dev)
@@ -176,14 +179,14 @@ def main():
         zz.zigzag_permute(plan, q, q_zz)
         zz.zigzag_permute(plan, k, k_zz)
         zz.zigzag_permute(plan, v, v_zz)
-        if w.backward:
+        if backward:
             zz.zigzag_permute(plan, do, do_zz)
         for s in range(cp):
             launch("fwd_step", lambda s=s: zz.varlen_ring_step_fwd(plan, zz.ALL_RANKS, s, q_zz, k_zz, v_zz,
                                                                    o_acc, lse, merge=s > 0))
         zz.finalize_fwd(plan, o_acc, unpermute=False, out=o_zz)
         zz.zigzag_unpermute(plan, o_zz, o)
-        if not w.backward:
+        if not backward:
             return
         zz.bwd_preprocess(plan, o_zz, do_zz, delta)
         for s in range(cp):
@@ -228,7 +231,7 @@ def main():
         traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", "c5_hbm_traffic.txt"), dom + "_kernel")
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     fwd_ms = ks["fwd_step"]["total_ms"] / args.steps
-    bwd_ms = (ks["bwd_dkv"]["total_ms"] + ks["bwd_dq"]["total_ms"]) / args.steps if w.backward else 0.0
+    bwd_ms = (ks["bwd_dkv"]["total_ms"] + ks["bwd_dq"]["total_ms"]) / args.steps if backward else 0.0
 
     balance = None
     if not args.no_balance:
@@ -260,7 +263,7 @@ def main():
         cpu = cpu_baseline(w, q, k, v, args.cpu_budget)
 
     out = {
-        "metric": "useful attention TFLOP/s (fwd+bwd) and % of bf16 MFMA peak, 1 MI355X",
+        "metric": "useful attention TFLOP/s (%s) and %% of bf16 MFMA peak, 1 MI355X" % ("fwd+bwd" if backward else "fwd"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -275,13 +278,13 @@ def main():
         "config": {
             "workload": "%s: %s, %d tokens, lengths %s, GQA %d/%d, head_dim %d, simulated CP=%d zigzag, %s"
                         % (w.name, w.dtype, T, ("%d sequences" % (len(cu) - 1)) if len(cu) > 2 else "one causal sequence",
-                           hq, hkv, d, cp, "forward + backward" if w.backward else "forward"),
+                           hq, hkv, d, cp, "forward + backward" if backward else "forward"),
             "tokens": T, "heads_q": hq, "heads_kv": hkv, "head_dim": d, "cp": cp,
             "parallelism": "cp%d simulated on 1 GPU" % cp,
         },
         "pct_of_peak": round(100.0 * value / peak, 2),
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
-        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if w.backward else None,
+        "bwd_tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2) if backward else None,
         "useful_fwd_tflop": round(fwd_flops / 1e12, 3),
         "tile_efficiency": round(useful_pairs / issued_pairs, 4),
         "kernels_ms": {n: round(v["mean_ms"], 4) for n, v in ks.items()},

@@ -100,8 +100,11 @@ def test_forward_zero_query_closed_form_full_size(name):
     assert worst_l < 1e-4
 
 
-def test_backward_c5_sampled_dq_rows():
-    w, cu, plan, (q, k, v, do), (qz, kz, vz, doz) = setup("c5", with_do=True)
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_backward_sampled_dq_rows(name):
+    """c4: 65536 tokens packed from 15 documents (document mask), GQA 64/8;
+    c5: one 131072-token sequence, GQA 64/8."""
+    w, cu, plan, (q, k, v, do), (qz, kz, vz, doz) = setup(name, with_do=True)
     o_acc, lse, _ = forward(plan, qz, kz, vz)
     o_zz = zz.finalize_fwd(plan, o_acc)
     dq, dk, dv = zz.ring_attention_bwd(plan, qz, kz, vz, o_zz, doz, lse)
@@ -114,12 +117,14 @@ def test_backward_c5_sampled_dq_rows():
     assert rel_l2(got, want) < TOL_BF16["rel"]
 
 
-def test_backward_c5_gradient_identities():
-    """Exact identities of the attention gradient, per key/value group:
+@pytest.mark.parametrize("name", ["c4", "c5"])
+def test_backward_gradient_identities(name):
+    """Exact identities of the attention gradient, per key/value group (they
+    hold per document, hence also summed over a packed batch):
     sum_k dK_k = 0;  sum_k dV_k = sum over the group's heads of sum_q dO_q;
     sum over heads of <Q, dQ> = <K, dK>."""
     import torch
-    w, cu, plan, (q, k, v, do), (qz, kz, vz, doz) = setup("c5", with_do=True)
+    w, cu, plan, (q, k, v, do), (qz, kz, vz, doz) = setup(name, with_do=True)
     o_acc, lse, _ = forward(plan, qz, kz, vz)
     o_zz = zz.finalize_fwd(plan, o_acc)
     dq, dk, dv = zz.ring_attention_bwd(plan, qz, kz, vz, o_zz, doz, lse)
@@ -155,6 +160,38 @@ def test_backward_c5_zero_key_closed_form():
     got = dv[dst].double()
     err = float((got - want).abs().max())
     assert err < 2e-3 * max(1.0, float(want.abs().max()))
+
+
+def test_backward_c4_one_head_full():
+    """Document-masked backward at full size (65536 tokens, 15 documents):
+    with dO zero for every query head but one, that head's dQ and its
+    group's dK, dV are the one-head gradients, compared in full against the
+    oracle's backward of that head alone."""
+    import torch
+    w, cu, plan, (q, k, v, do), (qz, kz, vz, doz) = setup("c4", with_do=True)
+    G = w.hq // w.hkv
+    h = w.hq - 3
+    g = h // G
+    keep = torch.zeros((1, w.hq, 1), dtype=doz.dtype, device=doz.device)
+    keep[0, h, 0] = 1
+    doz = doz * keep
+    do_h = do[:, h:h + 1]
+    o_acc, lse, _ = forward(plan, qz, kz, vz)
+    o_zz = zz.finalize_fwd(plan, o_acc)
+    dq, dk, dv = zz.ring_attention_bwd(plan, qz, kz, vz, o_zz, doz, lse)
+    want = oracle.attn_bwd(q[:, h:h + 1], k[:, g:g + 1], v[:, g:g + 1], do_h, cu, w.scale)
+    dst = torch.as_tensor(plan.zigzag_dst(), device="cuda")
+    got = (dq[dst][:, h], dk[dst][:, g], dv[dst][:, g])
+    for nm, gt, wt in zip(("dq", "dk", "dv"), got, want):
+        gt = gt.float().cpu().numpy()
+        wt = wt[:, 0]
+        gate = TOL_BF16["abs"] * max(1.0, float(np.abs(wt).max()))
+        assert max_abs(gt, wt) < gate, (nm, max_abs(gt, wt), gate)
+        assert rel_l2(gt, wt) < TOL_BF16["rel"], (nm, rel_l2(gt, wt))
+    # the other query heads of the group contribute nothing, the other
+    # groups nothing at all
+    others = [x for x in range(w.hkv) if x != g]
+    assert float(dk[:, others].abs().max()) == 0.0 and float(dv[:, others].abs().max()) == 0.0
 
 
 def test_debug_mask_c3_sampled_steps():
