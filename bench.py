@@ -127,6 +127,8 @@ def main():
     ap.add_argument("--no-balance", action="store_true")
     ap.add_argument("--with-backward", action="store_true",
                     help="also time the backward on a forward-only workload (synthetic dO)")
+    ap.add_argument("--gathered", action="store_true",
+                    help="forward as one launch against all K/V shards (no step partials or merges)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -181,9 +183,12 @@ def main():
         zz.zigzag_permute(plan, v, v_zz)
         if backward:
             zz.zigzag_permute(plan, do, do_zz)
-        for s in range(cp):
-            launch("fwd_step", lambda s=s: zz.varlen_ring_step_fwd(plan, zz.ALL_RANKS, s, q_zz, k_zz, v_zz,
-                                                                   o_acc, lse, merge=s > 0))
+        if args.gathered:
+            launch("fwd_gathered", lambda: zz.varlen_gathered_fwd(plan, zz.ALL_RANKS, q_zz, k_zz, v_zz, o_acc, lse))
+        else:
+            for s in range(cp):
+                launch("fwd_step", lambda s=s: zz.varlen_ring_step_fwd(plan, zz.ALL_RANKS, s, q_zz, k_zz, v_zz,
+                                                                       o_acc, lse, merge=s > 0))
         zz.finalize_fwd(plan, o_acc, unpermute=False, out=o_zz)
         zz.zigzag_unpermute(plan, o_zz, o)
         if not backward:
@@ -218,6 +223,7 @@ def main():
     ks = tm.summary()
     per_launch = {
         "fwd_step": 4.0 * d * hq * useful_pairs / cp,
+        "fwd_gathered": 4.0 * d * hq * useful_pairs,
         "bwd_dkv": 8.0 * d * hq * useful_pairs / cp,
         "bwd_dq": 6.0 * d * hq * useful_pairs / cp,
     }
@@ -230,11 +236,11 @@ def main():
         from zigzag_ring_attention_amd import profiling
         traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", "c5_hbm_traffic.txt"), dom + "_kernel")
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    fwd_ms = ks["fwd_step"]["total_ms"] / args.steps
+    fwd_ms = ks["fwd_gathered" if args.gathered else "fwd_step"]["total_ms"] / args.steps
     bwd_ms = (ks["bwd_dkv"]["total_ms"] + ks["bwd_dq"]["total_ms"]) / args.steps if backward else 0.0
 
     balance = None
-    if not args.no_balance:
+    if not args.no_balance and not args.gathered:
         # Each rank's forward steps run alone; ranks are timed in ascending and
         # then descending order and averaged, so clock or cache drift over the
         # measurement does not masquerade as imbalance.
@@ -278,7 +284,8 @@ def main():
         "config": {
             "workload": "%s: %s, %d tokens, lengths %s, GQA %d/%d, head_dim %d, simulated CP=%d zigzag, %s"
                         % (w.name, w.dtype, T, ("%d sequences" % (len(cu) - 1)) if len(cu) > 2 else "one causal sequence",
-                           hq, hkv, d, cp, "forward + backward" if backward else "forward"),
+                           hq, hkv, d, cp, ("forward + backward" if backward else "forward")
+                           + (", gathered K/V forward" if args.gathered else "")),
             "tokens": T, "heads_q": hq, "heads_kv": hkv, "head_dim": d, "cp": cp,
             "parallelism": "cp%d simulated on 1 GPU" % cp,
         },

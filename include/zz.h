@@ -178,6 +178,24 @@ zz_status zz_varlen_ring_step_fwd(const zz_plan *plan, int32_t rank, int32_t ste
                                   float *o_acc, float *lse_acc, int32_t merge, void *stream);
 
 /*
+ * Forward of rank r's queries against every shard at once (ring-attention-
+ * pytorch issue #20, "Zigzag attention support?": the maintainer reads the
+ * zigzag scheme as an all-gather of keys and values across ranks, which GQA
+ * makes affordable, and plans to offer that gather as an option).  With all
+ * K/V resident, each query row's visible keys are walked in one launch with
+ * one online softmax: no step partials and no merges.
+ *  rank        0..cp-1, or ZZ_ALL_RANKS.
+ *  q_zz, k_zz, v_zz  as zz_varlen_ring_step_fwd (whole zigzag buffers).
+ *  o           fp32 [T, hq, d]: normalized output of the launched ranks' rows.
+ *  lse         fp32 [hq, T]: natural-log LSE of the same rows.
+ * The result equals the merged ring forward up to rounding order (the same
+ * tiles are visited, grouped per row instead of per step).
+ * Errors: ZZ_ERR_ARG, ZZ_ERR_ALIGN, ZZ_ERR_STATE, ZZ_ERR_HIP.
+ */
+zz_status zz_varlen_gathered_fwd(const zz_plan *plan, int32_t rank, const void *q_zz, const void *k_zz,
+                                 const void *v_zz, float *o, float *lse, void *stream);
+
+/*
  * Standalone log-sum-exp merge: (o_acc, lse_acc) <- merge with (o_part,
  * lse_part).  o: fp32 [rows, heads, head_dim]; lse: fp32 [heads, rows].
  * (0, -inf) is the identity; two -inf rows give (0, -inf).

@@ -22,6 +22,7 @@ __all__ = [
     "finalize_fwd", "bwd_preprocess", "varlen_ring_step_bwd", "varlen_ring_step_bwd_dkv",
     "varlen_ring_step_bwd_dq", "finalize_bwd", "debug_mask",
     "ring_attention_fwd", "ring_attention_bwd", "library_path",
+    "varlen_gathered_fwd", "gathered_attention_fwd",
 ]
 
 PASS_FWD, PASS_BWD_DQ, PASS_BWD_DKV = 0, 1, 2
@@ -69,6 +70,7 @@ def lib():
         "zz_zigzag_permute": ([P, P, P, i64, P], i32),
         "zz_zigzag_unpermute": ([P, P, P, i64, P], i32),
         "zz_varlen_ring_step_fwd": ([P, i32, i32, P, P, P, P, P, i32, P], i32),
+        "zz_varlen_gathered_fwd": ([P, i32, P, P, P, P, P, P], i32),
         "zz_lse_merge": ([P, P, P, P, i64, i32, i32, P], i32),
         "zz_finalize_fwd": ([P, P, P, i32, P], i32),
         "zz_bwd_preprocess": ([P, P, P, P, P], i32),
@@ -247,6 +249,26 @@ def varlen_ring_step_fwd(plan: Plan, rank: int, step: int, q_zz, k_zz, v_zz, o_a
     _check(lib().zz_varlen_ring_step_fwd(plan.handle, rank, step, _ptr(q_zz), _ptr(k_zz), _ptr(v_zz),
                                          _ptr(o_acc), _ptr(lse_acc), 1 if merge else 0, _stream(stream)),
            "zz_varlen_ring_step_fwd")
+
+
+def varlen_gathered_fwd(plan: Plan, rank: int, q_zz, k_zz, v_zz, o, lse, stream=None):
+    """Forward of rank `rank` (or ALL_RANKS) against every shard in one launch:
+    writes the normalized O (fp32 [T,hq,d]) and LSE (fp32 [hq,T]) of its rows."""
+    _check_qkv(plan, q_zz, k_zz, v_zz)
+    _check_acc(plan, o, lse)
+    _check(lib().zz_varlen_gathered_fwd(plan.handle, rank, _ptr(q_zz), _ptr(k_zz), _ptr(v_zz), _ptr(o),
+                                        _ptr(lse), _stream(stream)), "zz_varlen_gathered_fwd")
+
+
+def gathered_attention_fwd(plan: Plan, q_zz, k_zz, v_zz, rank: int = ALL_RANKS, o=None, lse=None, stream=None):
+    """The all-gather alternative to the ring forward: every rank's queries
+    against all K/V at once.  Returns (o fp32 [T,hq,d], lse fp32 [hq,T])."""
+    import torch
+    dev = q_zz.device
+    o = torch.empty((plan.total, plan.hq, plan.d), dtype=torch.float32, device=dev) if o is None else o
+    lse = torch.empty((plan.hq, plan.total), dtype=torch.float32, device=dev) if lse is None else lse
+    varlen_gathered_fwd(plan, rank, q_zz, k_zz, v_zz, o, lse, stream)
+    return o, lse
 
 
 def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):

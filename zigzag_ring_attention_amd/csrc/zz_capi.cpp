@@ -212,6 +212,15 @@ zz_status zz_varlen_ring_step_fwd(const zz_plan *p, int32_t rank, int32_t step, 
                                           (hipStream_t)stream), "varlen_ring_step_fwd");
 }
 
+zz_status zz_varlen_gathered_fwd(const zz_plan *p, int32_t rank, const void *q_zz, const void *k_zz,
+                                 const void *v_zz, float *o, float *lse, void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_rank_step(p, rank, 0, true));
+    ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, o, lse}));
+    return hip_status(zz::launch_fwd_gathered(p, rank, q_zz, k_zz, v_zz, o, lse, (hipStream_t)stream),
+                      "varlen_gathered_fwd");
+}
+
 zz_status zz_lse_merge(float *o_acc, float *lse_acc, const float *o_part, const float *lse_part,
                        int64_t rows, int32_t heads, int32_t head_dim, void *stream) {
     ZZ_TRY(check_ptrs({o_acc, lse_acc, o_part, lse_part}));

@@ -219,11 +219,11 @@ fwd_step_kernel(FwdArgs a) {
 }
 
 template <typename T, int D>
-hipError_t launch_t(const zz_plan *p, const Launch &L, const void *q, const void *k, const void *v, float *o,
-                    float *lse, int merge, hipStream_t st) {
+hipError_t launch_t(const zz_plan *p, const Launch &L, const TileRec *tiles, const void *q, const void *k,
+                    const void *v, float *o, float *lse, int merge, hipStream_t st) {
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.items = L.items; a.order = L.order; a.tiles = dev_tiles(p, ZZ_PASS_FWD);
+    a.items = L.items; a.order = L.order; a.tiles = tiles;
     a.T = p->T; a.n = (int32_t)(p->T / p->cp); a.hq = p->hq; a.hkv = p->hkv;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
     a.merge = merge;
@@ -232,20 +232,31 @@ hipError_t launch_t(const zz_plan *p, const Launch &L, const void *q, const void
     return hipGetLastError();
 }
 
+hipError_t launch_fwd_pass(const zz_plan *p, int pass, int rank, int step, const void *q, const void *k,
+                           const void *v, float *o, float *lse, int merge, hipStream_t st) {
+    const Launch L = launch_items(p, pass, rank, step);
+    if (L.n == 0) return hipSuccess;
+    const TileRec *tiles = dev_tiles(p, pass);
+    if (p->dtype == ZZ_BF16) {
+        if (p->d == 32) return launch_t<bf16, 32>(p, L, tiles, q, k, v, o, lse, merge, st);
+        if (p->d == 64) return launch_t<bf16, 64>(p, L, tiles, q, k, v, o, lse, merge, st);
+        return launch_t<bf16, 128>(p, L, tiles, q, k, v, o, lse, merge, st);
+    }
+    if (p->d == 32) return launch_t<float, 32>(p, L, tiles, q, k, v, o, lse, merge, st);
+    if (p->d == 64) return launch_t<float, 64>(p, L, tiles, q, k, v, o, lse, merge, st);
+    return launch_t<float, 128>(p, L, tiles, q, k, v, o, lse, merge, st);
+}
+
 }  // namespace
 
 hipError_t launch_fwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k, const void *v,
                            float *o, float *lse, int merge, hipStream_t st) {
-    const Launch L = launch_items(p, ZZ_PASS_FWD, rank, step);
-    if (L.n == 0) return hipSuccess;
-    if (p->dtype == ZZ_BF16) {
-        if (p->d == 32) return launch_t<bf16, 32>(p, L, q, k, v, o, lse, merge, st);
-        if (p->d == 64) return launch_t<bf16, 64>(p, L, q, k, v, o, lse, merge, st);
-        return launch_t<bf16, 128>(p, L, q, k, v, o, lse, merge, st);
-    }
-    if (p->d == 32) return launch_t<float, 32>(p, L, q, k, v, o, lse, merge, st);
-    if (p->d == 64) return launch_t<float, 64>(p, L, q, k, v, o, lse, merge, st);
-    return launch_t<float, 128>(p, L, q, k, v, o, lse, merge, st);
+    return launch_fwd_pass(p, ZZ_PASS_FWD, rank, step, q, k, v, o, lse, merge, st);
+}
+
+hipError_t launch_fwd_gathered(const zz_plan *p, int rank, const void *q, const void *k, const void *v, float *o,
+                               float *lse, hipStream_t st) {
+    return launch_fwd_pass(p, kPassGathered, rank, 0, q, k, v, o, lse, 0, st);
 }
 
 }  // namespace zz

@@ -55,7 +55,10 @@ struct zz_plan {
     zz_dtype dtype = ZZ_BF16;
     std::vector<int32_t> cu;     // packed cu_seqlens
     std::vector<int32_t> src;    // zigzag row -> packed token
-    zz::PassTables pass[3];
+    // pass[ZZ_PASS_FWD..ZZ_PASS_BWD_DKV] are the ring passes; pass[kPassGathered]
+    // is the forward against every shard at once (one "step": its rank_off
+    // has cp+1 entries, its order_off 2).
+    zz::PassTables pass[4];
     size_t off_src = 0;
     size_t ws_bytes = 0;
     std::vector<uint8_t> image;  // host image of the device workspace
@@ -68,6 +71,9 @@ namespace zz {
 zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, int32_t hkv,
                      int32_t d, zz_dtype dt, int32_t bm, int32_t bn, zz_plan **out,
                      std::string *err);
+
+// Internal pass index of the gathered forward (not a public zz_pass value).
+constexpr int kPassGathered = 3;
 
 // Device-side pointers into a bound plan's workspace.
 inline const int32_t *dev_src(const zz_plan *p) {
@@ -103,6 +109,10 @@ hipError_t launch_bwd_pre(const zz_plan *p, const void *o, const void *dout, flo
                           hipStream_t st);
 hipError_t launch_debug_mask(const zz_plan *p, int pass, int rank, int step, uint8_t *mask,
                              hipStream_t st);
+// Forward of rank (or all ranks) against every shard in one launch: writes
+// the normalised O and the LSE, no merge.
+hipError_t launch_fwd_gathered(const zz_plan *p, int rank, const void *q, const void *k, const void *v,
+                               float *o, float *lse, hipStream_t st);
 hipError_t launch_fwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k,
                            const void *v, float *o, float *lse, int merge, hipStream_t st);
 // which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.

@@ -149,6 +149,75 @@ void build_pass(zz_plan *p, PassTables &t) {
     t.order_off[cp] = (int64_t)t.order.size();
 }
 
+// Gathered forward: every query item of rank r lists the visible tiles of
+// every shard, with key rows given in the global zigzag order (shard j's rows
+// start at j*T/cp), so the items carry shard 0 and one launch computes the
+// whole causal softmax of each row -- the all-gather alternative to the ring
+// (ring-attention-pytorch issue #20, "Zigzag attention support?": the
+// maintainer reads the scheme as gathering keys and values across ranks,
+// which GQA makes affordable, and plans to offer that gather as an option).
+void build_gathered_pass(zz_plan *p, PassTables &t) {
+    const int32_t cp = p->cp;
+    const int64_t n = p->T / cp;
+    t.items.clear();
+    t.tiles.clear();
+    t.order.clear();
+    t.rank_off.assign((size_t)cp + 1, 0);
+    t.order_off.assign(2, 0);
+    t.useful.assign((size_t)cp, 0);
+    t.issued.assign((size_t)cp, 0);
+    std::vector<int64_t> item_work;
+    for (int32_t r = 0; r < cp; ++r) {
+        t.rank_off[(size_t)r] = (int64_t)t.items.size();
+        const size_t first_item = t.items.size();
+        auto qch = local_chunks(p->cu, cp, r);
+        std::vector<std::vector<std::vector<Chunk>>> kch((size_t)cp);
+        for (int32_t j = 0; j < cp; ++j) kch[(size_t)j] = local_chunks(p->cu, cp, j);
+        for (int32_t i = 0; i < p->nseq; ++i) {
+            for (const Chunk &a : qch[(size_t)i]) {
+                for (int32_t a0 = 0; a0 < a.len; a0 += t.bm) {
+                    const int32_t a1 = std::min(a0 + t.bm, a.len);
+                    WorkItem it{r, 0, a.start + a0, a.start + a1, (int32_t)t.tiles.size(), 0, 0, 0};
+                    int64_t work = 0;
+                    for (int32_t j = 0; j < cp; ++j) {
+                        for (const Chunk &b : kch[(size_t)j][(size_t)i]) {
+                            for (int32_t b0 = 0; b0 < b.len; b0 += t.bn) {
+                                const int32_t b1 = std::min(b0 + t.bn, b.len);
+                                int32_t delta;
+                                const int kind = classify(a.index, a0, a1, b.index, b0, b1, &delta);
+                                if (!kind) continue;
+                                const int32_t g0 = (int32_t)(j * n + b.start + b0), g1 = (int32_t)(j * n + b.start + b1);
+                                t.tiles.push_back(TileRec{g0, g1, kind, delta});
+                                const int64_t area = (int64_t)(a1 - a0) * (b1 - b0);
+                                work += area;
+                                t.issued[(size_t)r] += area;
+                                t.useful[(size_t)r] += tile_pairs(kind, a0, a1, b0, b1, delta);
+                            }
+                        }
+                    }
+                    it.tend = (int32_t)t.tiles.size();
+                    t.items.push_back(it);   // every query row gets its O and LSE written
+                    item_work.push_back(work);
+                }
+            }
+        }
+        std::vector<size_t> idx(t.items.size() - first_item);
+        for (size_t u = 0; u < idx.size(); ++u) idx[u] = first_item + u;
+        std::stable_sort(idx.begin(), idx.end(), [&](size_t x, size_t y) { return item_work[x] > item_work[y]; });
+        std::vector<WorkItem> tmp;
+        std::vector<int64_t> tw;
+        for (size_t u : idx) { tmp.push_back(t.items[u]); tw.push_back(item_work[u]); }
+        std::copy(tmp.begin(), tmp.end(), t.items.begin() + first_item);
+        std::copy(tw.begin(), tw.end(), item_work.begin() + first_item);
+    }
+    t.rank_off[(size_t)cp] = (int64_t)t.items.size();
+    std::vector<int32_t> ord;
+    for (size_t u = 0; u < t.items.size(); ++u) ord.push_back((int32_t)u);
+    std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return item_work[x] > item_work[y]; });
+    t.order = ord;
+    t.order_off[1] = (int64_t)t.order.size();
+}
+
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -205,7 +274,10 @@ zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, in
     // LDS stage of the dK/dV kernel fits.
     dkv.bm = (dt == ZZ_F32 && d >= 64) ? 32 : 64;
     dkv.bn = 128; dkv.key_major = true; dkv.keep_empty = false;
-    for (auto &t : p->pass) build_pass(p, t);
+    PassTables &ga = p->pass[kPassGathered];
+    ga.bm = bm; ga.bn = bn; ga.key_major = false; ga.keep_empty = true;
+    for (int k = ZZ_PASS_FWD; k <= ZZ_PASS_BWD_DKV; ++k) build_pass(p, p->pass[k]);
+    build_gathered_pass(p, ga);
 
     // Workspace image: zigzag map, then items / tiles / order of each pass.
     size_t off = 0;

@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
     python -m zigzag_ring_attention_amd.profiling stats  <kernel_stats.csv> <command...>
-    python -m zigzag_ring_attention_amd.profiling traffic <fetch.csv> <write.csv> <command...>
+    python -m zigzag_ring_attention_amd.profiling traffic <fetch.csv> <write.csv> [--workload=cN] <command...>
     python -m zigzag_ring_attention_amd.profiling util <counter_collection.csv> <command...>
 
 ``stats`` turns a ``--kernel-trace --stats`` kernel_stats.csv into a markdown
@@ -164,10 +164,16 @@ if __name__ == "__main__":
     elif sys.argv[1] == "util":
         sys.stdout.write(util_markdown(sys.argv[2], " ".join(sys.argv[3:])))
     elif sys.argv[1] == "traffic":
-        # copy size of the first permute: Q of the 131072-token, 64-head, d=128 bf16 workload
+        # copy size of the first permute of a bench step: Q of the workload
+        # (c5 unless "--workload cN" follows the two files)
         import synthetic
-        w = synthetic.WORKLOADS["c5"]
-        copy_bytes = float(w.total * w.hq * w.d * 2)
-        sys.stdout.write(traffic_text(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]), copy_bytes))
+        rest = sys.argv[4:]
+        name = "c5"
+        if rest and rest[0].startswith("--workload="):
+            name = rest[0].split("=", 1)[1]
+            rest = rest[1:]
+        w = synthetic.WORKLOADS[name]
+        copy_bytes = float(w.total * w.hq * w.d * (2 if w.dtype == "bf16" else 4))
+        sys.stdout.write(traffic_text(sys.argv[2], sys.argv[3], " ".join(rest), copy_bytes))
     else:
         raise SystemExit("usage: profiling.py stats|traffic ...")
