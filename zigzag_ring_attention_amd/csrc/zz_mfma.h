@@ -176,36 +176,43 @@ template <int D> struct Mfma<bf16, D> {
     // accumulator dependency stalls the matrix unit.
     static __device__ __forceinline__ void gemm_rows_lds2(f32x16 &acc0, f32x16 &acc1, const bf16 *tile, int row0,
                                                           int row1, const Op (&op)[KS], int hh) {
-        bf16x8 a0 = row_frag(tile, row0, 0, hh), a1 = row_frag(tile, row1, 0, hh);
+        // operands of step ks + PF are read while step ks multiplies
+        constexpr int PF = KS >= 4 ? 2 : 1;
+        bf16x8 a0[PF + 1], a1[PF + 1];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            a0[j] = row_frag(tile, row0, j, hh);
+            a1[j] = row_frag(tile, row1, j, hh);
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 n0 = a0, n1 = a1;
-            if (ks + 1 < KS) {
-                n0 = row_frag(tile, row0, ks + 1, hh);
-                n1 = row_frag(tile, row1, ks + 1, hh);
+            if (ks + PF < KS) {
+                a0[(ks + PF) % (PF + 1)] = row_frag(tile, row0, ks + PF, hh);
+                a1[(ks + PF) % (PF + 1)] = row_frag(tile, row1, ks + PF, hh);
             }
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, op[ks], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, op[ks], acc1, 0, 0, 0);
-            a0 = n0;
-            a1 = n1;
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks % (PF + 1)], op[ks], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks % (PF + 1)], op[ks], acc1, 0, 0, 0);
         }
     }
     // Two chains with their own tiles and operands (same rows).
     static __device__ __forceinline__ void gemm_rows_lds_pair(f32x16 &acc0, const bf16 *tile0, const Op (&op0)[KS],
                                                               f32x16 &acc1, const bf16 *tile1, const Op (&op1)[KS],
                                                               int row, int hh) {
-        bf16x8 a0 = row_frag(tile0, row, 0, hh), a1 = row_frag(tile1, row, 0, hh);
+        constexpr int PF = KS >= 4 ? 2 : 1;
+        bf16x8 a0[PF + 1], a1[PF + 1];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) {
+            a0[j] = row_frag(tile0, row, j, hh);
+            a1[j] = row_frag(tile1, row, j, hh);
+        }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 n0 = a0, n1 = a1;
-            if (ks + 1 < KS) {
-                n0 = row_frag(tile0, row, ks + 1, hh);
-                n1 = row_frag(tile1, row, ks + 1, hh);
+            if (ks + PF < KS) {
+                a0[(ks + PF) % (PF + 1)] = row_frag(tile0, row, ks + PF, hh);
+                a1[(ks + PF) % (PF + 1)] = row_frag(tile1, row, ks + PF, hh);
             }
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, op0[ks], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, op1[ks], acc1, 0, 0, 0);
-            a0 = n0;
-            a1 = n1;
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks % (PF + 1)], op0[ks], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks % (PF + 1)], op1[ks], acc1, 0, 0, 0);
         }
     }
     // A operand of X^T for one 32x32x16 step over 16 contraction rows of a
