@@ -129,7 +129,8 @@ def main():
     ap.add_argument("--with-backward", action="store_true",
                     help="also time the backward on a forward-only workload (synthetic dO)")
     ap.add_argument("--gathered", action="store_true",
-                    help="forward as one launch against all K/V shards (no step partials or merges)")
+                    help="the all-gather form: forward and backward as one launch (per kernel) against "
+                         "all shards, no step partials, merges or accumulation")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -189,6 +190,11 @@ def main():
         if not backward:
             return
         zz.bwd_preprocess(plan, o_zz, do_zz, delta)
+        if args.gathered:
+            launch("bwd_gathered", lambda: zz.varlen_gathered_bwd(plan, zz.ALL_RANKS, q_zz, k_zz, v_zz, do_zz, lse,
+                                                                  delta, dq_acc, dk_acc, dv_acc))
+            zz.finalize_bwd(plan, dq_acc, dk_acc, dv_acc, unpermute=False, out=grads)
+            return
         for s in range(cp):
             launch("bwd_dkv", lambda s=s: zz.varlen_ring_step_bwd_dkv(
                 plan, zz.ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dk_acc, dv_acc, accumulate=s > 0))
@@ -243,6 +249,7 @@ def main():
     per_launch = {
         "fwd_step": 4.0 * d * hq * useful_pairs / cp,
         "fwd_gathered": 4.0 * d * hq * useful_pairs,
+        "bwd_gathered": 14.0 * d * hq * useful_pairs,
         "bwd_dkv": 8.0 * d * hq * useful_pairs / cp,
         "bwd_dq": 6.0 * d * hq * useful_pairs / cp,
     }
@@ -256,7 +263,12 @@ def main():
         traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", "c5_hbm_traffic.txt"), dom + "_kernel")
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     fwd_ms = ks["fwd_gathered" if args.gathered else "fwd_step"]["total_ms"] / args.steps
-    bwd_ms = (ks["bwd_dkv"]["total_ms"] + ks["bwd_dq"]["total_ms"]) / args.steps if backward else 0.0
+    if not backward:
+        bwd_ms = 0.0
+    elif args.gathered:
+        bwd_ms = ks["bwd_gathered"]["total_ms"] / args.steps
+    else:
+        bwd_ms = (ks["bwd_dkv"]["total_ms"] + ks["bwd_dq"]["total_ms"]) / args.steps
 
     balance = None
     if not args.no_balance and not args.gathered:
@@ -304,7 +316,7 @@ def main():
             "workload": "%s: %s, %d tokens, lengths %s, GQA %d/%d, head_dim %d, simulated CP=%d zigzag, %s"
                         % (w.name, w.dtype, T, ("%d sequences" % (len(cu) - 1)) if len(cu) > 2 else "one causal sequence",
                            hq, hkv, d, cp, ("forward + backward" if backward else "forward")
-                           + (", gathered K/V forward" if args.gathered else "")),
+                           + (", all-gather K/V form" if args.gathered else "")),
             "tokens": T, "heads_q": hq, "heads_kv": hkv, "head_dim": d, "cp": cp,
             "parallelism": "cp%d simulated on 1 GPU" % cp,
         },

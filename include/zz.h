@@ -196,6 +196,23 @@ zz_status zz_varlen_gathered_fwd(const zz_plan *plan, int32_t rank, const void *
                                  const void *v_zz, float *o, float *lse, void *stream);
 
 /*
+ * Backward of the gathered form (same passage as zz_varlen_gathered_fwd):
+ * rank r's dQ rows against every shard, and the dK, dV rows of shard r
+ * against every rank's queries, one launch per kernel, no per-step
+ * accumulation.
+ *  rank        0..cp-1 (its query rows and its own K/V shard), or ZZ_ALL_RANKS.
+ *  q_zz, k_zz, v_zz, do_zz, lse, delta  as zz_varlen_ring_step_bwd (lse from
+ *              the forward, delta from zz_bwd_preprocess).
+ *  dq fp32 [T, hq, d]; dk, dv fp32 [T, hkv, d]: the launched rows are
+ *              written (not accumulated).
+ * The result equals the sum over the ring steps up to rounding order.
+ * Errors: ZZ_ERR_ARG, ZZ_ERR_ALIGN, ZZ_ERR_STATE, ZZ_ERR_HIP.
+ */
+zz_status zz_varlen_gathered_bwd(const zz_plan *plan, int32_t rank, const void *q_zz, const void *k_zz,
+                                 const void *v_zz, const void *do_zz, const float *lse, const float *delta,
+                                 float *dq, float *dk, float *dv, void *stream);
+
+/*
  * Standalone log-sum-exp merge: (o_acc, lse_acc) <- merge with (o_part,
  * lse_part).  o: fp32 [rows, heads, head_dim]; lse: fp32 [heads, rows].
  * (0, -inf) is the identity; two -inf rows give (0, -inf).

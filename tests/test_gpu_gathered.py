@@ -82,3 +82,68 @@ def test_gathered_forward_c4_full_size():
     assert max_abs(got_o, want_o) < TOL["bf16"]["abs"]
     assert rel_l2(got_o, want_o) < TOL["bf16"]["rel"]
     assert max_abs(got_lse, want_lse) < TOL["bf16"]["lse"]
+
+
+# ------------------------------------------------------------------ backward
+
+def gathered_grads(case):
+    o, lse = zz.gathered_attention_fwd(case.plan, case.qz, case.kz, case.vz)
+    o_zz = zz.finalize_fwd(case.plan, o)
+    dq, dk, dv = zz.gathered_attention_bwd(case.plan, case.qz, case.kz, case.vz, o_zz, case.doz, lse)
+    return [to_np(x)[case.dst] for x in (dq, dk, dv)]
+
+
+@pytest.mark.parametrize("lengths,cp,hq,hkv,d,dtype", [
+    ((96, 64, 96), 2, 2, 2, 32, "f32"),
+    ((8, 24, 16), 4, 4, 2, 64, "f32"),
+    ((200, 56), 2, 4, 2, 32, "f32"),
+    ((128, 256, 64), 2, 4, 2, 128, "bf16"),
+    ((16, 48, 528, 8), 4, 8, 1, 128, "bf16"),
+])
+def test_gathered_backward_matches_oracle(lengths, cp, hq, hkv, d, dtype):
+    case = Case(lengths, cp, hq, hkv, d, dtype, 37, with_do=True)
+    got = gathered_grads(case)
+    want = oracle.attn_bwd(case.q, case.k, case.v, case.do, case.cu, case.scale)
+    tol = TOL[dtype]
+    for name, g, w in zip(("dq", "dk", "dv"), got, want):
+        gate = tol["abs"] * max(1.0, float(np.abs(w).max()))
+        assert max_abs(g, w) < gate, (name, max_abs(g, w), gate)
+        assert rel_l2(g, w) < tol["rel"], (name, rel_l2(g, w))
+
+
+def test_gathered_backward_per_rank_equals_all_ranks():
+    import torch
+    case = Case((16, 48, 528, 8), 4, 8, 1, 128, "bf16", 9, with_do=True)
+    o, lse = zz.gathered_attention_fwd(case.plan, case.qz, case.kz, case.vz)
+    o_zz = zz.finalize_fwd(case.plan, o)
+    delta = zz.bwd_preprocess(case.plan, o_zz, case.doz)
+    outs = []
+    for ranks in ([zz.ALL_RANKS], list(range(case.cp))):
+        dq = torch.full((case.T, case.hq, case.d), 5.0, device="cuda")
+        dk = torch.full((case.T, case.hkv, case.d), 5.0, device="cuda")
+        dv = torch.full_like(dk, 5.0)
+        for r in ranks:
+            zz.varlen_gathered_bwd(case.plan, r, case.qz, case.kz, case.vz, case.doz, lse, delta, dq, dk, dv)
+        outs.append((dq, dk, dv))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_gathered_backward_c4_full_size_equals_ring():
+    """c4 at full size: the gathered backward against the sum of the ring
+    steps (same tiles grouped per item instead of per step)."""
+    import torch
+    w = synthetic.WORKLOADS["c4"]
+    cu = synthetic.cu_seqlens_for(w)
+    q, k, v, do = synthetic.randn_qkv(w.seed, w.total, w.hq, w.hkv, w.d, w.dtype, with_do=True)
+    plan = zz.Plan(cu, w.cp, w.hq, w.hkv, w.d, w.dtype, device="cuda")
+    qz, kz, vz, doz = (zz.zigzag_permute(plan, x.cuda()) for x in (q, k, v, do))
+    o_acc, lse = zz.ring_attention_fwd(plan, qz, kz, vz)
+    o_zz = zz.finalize_fwd(plan, o_acc)
+    ring = zz.ring_attention_bwd(plan, qz, kz, vz, o_zz, doz, lse)
+    gath = zz.gathered_attention_bwd(plan, qz, kz, vz, o_zz, doz, lse)
+    for name, a, b in zip(("dq", "dk", "dv"), gath, ring):
+        scale = max(1.0, float(b.abs().max()))
+        # both sum the same fp32 tile products, in a different order
+        assert float((a - b).abs().max()) < 1e-3 * scale, name
+        assert rel_l2(to_np(a), to_np(b)) < 1e-4, name

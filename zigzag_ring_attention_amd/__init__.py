@@ -22,7 +22,7 @@ __all__ = [
     "finalize_fwd", "bwd_preprocess", "varlen_ring_step_bwd", "varlen_ring_step_bwd_dkv",
     "varlen_ring_step_bwd_dq", "finalize_bwd", "debug_mask",
     "ring_attention_fwd", "ring_attention_bwd", "library_path",
-    "varlen_gathered_fwd", "gathered_attention_fwd",
+    "varlen_gathered_fwd", "gathered_attention_fwd", "varlen_gathered_bwd", "gathered_attention_bwd",
 ]
 
 PASS_FWD, PASS_BWD_DQ, PASS_BWD_DKV = 0, 1, 2
@@ -71,6 +71,7 @@ def lib():
         "zz_zigzag_unpermute": ([P, P, P, i64, P], i32),
         "zz_varlen_ring_step_fwd": ([P, i32, i32, P, P, P, P, P, i32, P], i32),
         "zz_varlen_gathered_fwd": ([P, i32, P, P, P, P, P, P], i32),
+        "zz_varlen_gathered_bwd": ([P, i32, P, P, P, P, P, P, P, P, P, P], i32),
         "zz_lse_merge": ([P, P, P, P, i64, i32, i32, P], i32),
         "zz_finalize_fwd": ([P, P, P, i32, P], i32),
         "zz_bwd_preprocess": ([P, P, P, P, P], i32),
@@ -269,6 +270,30 @@ def gathered_attention_fwd(plan: Plan, q_zz, k_zz, v_zz, rank: int = ALL_RANKS, 
     lse = torch.empty((plan.hq, plan.total), dtype=torch.float32, device=dev) if lse is None else lse
     varlen_gathered_fwd(plan, rank, q_zz, k_zz, v_zz, o, lse, stream)
     return o, lse
+
+
+def varlen_gathered_bwd(plan: Plan, rank: int, q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv,
+                        stream=None):
+    """Backward of the gathered form: dq rows of `rank` and dk/dv rows of its
+    shard (or every rank) against all the other side's rows, written in one
+    launch per kernel."""
+    _check_qkv(plan, q_zz, k_zz, v_zz)
+    _check(lib().zz_varlen_gathered_bwd(plan.handle, rank, _ptr(q_zz), _ptr(k_zz), _ptr(v_zz), _ptr(do_zz),
+                                        _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _stream(stream)),
+           "zz_varlen_gathered_bwd")
+
+
+def gathered_attention_bwd(plan: Plan, q_zz, k_zz, v_zz, o_zz, do_zz, lse, stream=None):
+    """Backward of the gathered form from the forward output O and its LSE.
+    Returns (dq fp32 [T,hq,d], dk, dv fp32 [T,hkv,d]) in the zigzag layout."""
+    import torch
+    dev = q_zz.device
+    delta = bwd_preprocess(plan, o_zz, do_zz, stream=stream)
+    dq = torch.empty((plan.total, plan.hq, plan.d), dtype=torch.float32, device=dev)
+    dk = torch.empty((plan.total, plan.hkv, plan.d), dtype=torch.float32, device=dev)
+    dv = torch.empty_like(dk)
+    varlen_gathered_bwd(plan, ALL_RANKS, q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv, stream)
+    return dq, dk, dv
 
 
 def lse_merge(o_acc, lse_acc, o_part, lse_part, stream=None):

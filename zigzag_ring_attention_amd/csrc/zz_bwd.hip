@@ -405,27 +405,26 @@ bwd_dq_kernel(BwdArgs a) {
 }
 
 template <typename T, int D>
-hipError_t launch_t(const zz_plan *p, int rank, int step, BwdArgs a, int which, hipStream_t st) {
-    const Launch Lkv = launch_items(p, ZZ_PASS_BWD_DKV, rank, step);
+hipError_t launch_t(const zz_plan *p, int base, int rank, int step, BwdArgs a, int which, hipStream_t st) {
+    const int pkv = base + ZZ_PASS_BWD_DKV, pq = base + ZZ_PASS_BWD_DQ;
+    const Launch Lkv = launch_items(p, pkv, rank, step);
     if ((which & 1) && Lkv.n > 0) {
-        a.items = Lkv.items; a.order = Lkv.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DKV); a.nitems = Lkv.n;
+        a.items = Lkv.items; a.order = Lkv.order; a.tiles = dev_tiles(p, pkv); a.nitems = Lkv.n;
         hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), dim3(Lkv.n * p->hkv), dim3(kDkvThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const Launch Lq = launch_items(p, ZZ_PASS_BWD_DQ, rank, step);
+    const Launch Lq = launch_items(p, pq, rank, step);
     if ((which & 2) && Lq.n > 0) {
-        a.items = Lq.items; a.order = Lq.order; a.tiles = dev_tiles(p, ZZ_PASS_BWD_DQ); a.nitems = Lq.n;
+        a.items = Lq.items; a.order = Lq.order; a.tiles = dev_tiles(p, pq); a.nitems = Lq.n;
         hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(Lq.n * p->hq), dim3(kDqThreads), 0, st, a);
     }
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_bwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k, const void *v,
-                           const void *dout, const float *lse, const float *delta, float *dq, float *dk,
-                           float *dv, int accumulate, int which, hipStream_t st) {
+hipError_t launch_bwd_pass(const zz_plan *p, int base, int rank, int step, const void *q, const void *k,
+                           const void *v, const void *dout, const float *lse, const float *delta, float *dq,
+                           float *dk, float *dv, int accumulate, int which, hipStream_t st) {
     BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = delta;
     a.dq = dq; a.dk = dk; a.dv = dv;
@@ -435,13 +434,27 @@ hipError_t launch_bwd_step(const zz_plan *p, int rank, int step, const void *q, 
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
     a.accumulate = accumulate;
     if (p->dtype == ZZ_BF16) {
-        if (p->d == 32) return launch_t<bf16, 32>(p, rank, step, a, which, st);
-        if (p->d == 64) return launch_t<bf16, 64>(p, rank, step, a, which, st);
-        return launch_t<bf16, 128>(p, rank, step, a, which, st);
+        if (p->d == 32) return launch_t<bf16, 32>(p, base, rank, step, a, which, st);
+        if (p->d == 64) return launch_t<bf16, 64>(p, base, rank, step, a, which, st);
+        return launch_t<bf16, 128>(p, base, rank, step, a, which, st);
     }
-    if (p->d == 32) return launch_t<float, 32>(p, rank, step, a, which, st);
-    if (p->d == 64) return launch_t<float, 64>(p, rank, step, a, which, st);
-    return launch_t<float, 128>(p, rank, step, a, which, st);
+    if (p->d == 32) return launch_t<float, 32>(p, base, rank, step, a, which, st);
+    if (p->d == 64) return launch_t<float, 64>(p, base, rank, step, a, which, st);
+    return launch_t<float, 128>(p, base, rank, step, a, which, st);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k, const void *v,
+                           const void *dout, const float *lse, const float *delta, float *dq, float *dk,
+                           float *dv, int accumulate, int which, hipStream_t st) {
+    return launch_bwd_pass(p, 0, rank, step, q, k, v, dout, lse, delta, dq, dk, dv, accumulate, which, st);
+}
+
+hipError_t launch_bwd_gathered(const zz_plan *p, int rank, const void *q, const void *k, const void *v,
+                               const void *dout, const float *lse, const float *delta, float *dq, float *dk,
+                               float *dv, hipStream_t st) {
+    return launch_bwd_pass(p, kPassGathered, rank, 0, q, k, v, dout, lse, delta, dq, dk, dv, 0, 3, st);
 }
 
 }  // namespace zz

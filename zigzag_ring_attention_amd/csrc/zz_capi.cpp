@@ -221,6 +221,16 @@ zz_status zz_varlen_gathered_fwd(const zz_plan *p, int32_t rank, const void *q_z
                       "varlen_gathered_fwd");
 }
 
+zz_status zz_varlen_gathered_bwd(const zz_plan *p, int32_t rank, const void *q_zz, const void *k_zz,
+                                 const void *v_zz, const void *do_zz, const float *lse, const float *delta,
+                                 float *dq, float *dk, float *dv, void *stream) {
+    ZZ_TRY(check_plan(p));
+    ZZ_TRY(check_rank_step(p, rank, 0, true));
+    ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv}));
+    return hip_status(zz::launch_bwd_gathered(p, rank, q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv,
+                                              (hipStream_t)stream), "varlen_gathered_bwd");
+}
+
 zz_status zz_lse_merge(float *o_acc, float *lse_acc, const float *o_part, const float *lse_part,
                        int64_t rows, int32_t heads, int32_t head_dim, void *stream) {
     ZZ_TRY(check_ptrs({o_acc, lse_acc, o_part, lse_part}));

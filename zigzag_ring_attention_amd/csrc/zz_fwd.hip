@@ -256,7 +256,7 @@ hipError_t launch_fwd_step(const zz_plan *p, int rank, int step, const void *q, 
 
 hipError_t launch_fwd_gathered(const zz_plan *p, int rank, const void *q, const void *k, const void *v, float *o,
                                float *lse, hipStream_t st) {
-    return launch_fwd_pass(p, kPassGathered, rank, 0, q, k, v, o, lse, 0, st);
+    return launch_fwd_pass(p, kPassGathered + ZZ_PASS_FWD, rank, 0, q, k, v, o, lse, 0, st);
 }
 
 }  // namespace zz

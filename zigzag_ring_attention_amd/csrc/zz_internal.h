@@ -55,10 +55,10 @@ struct zz_plan {
     zz_dtype dtype = ZZ_BF16;
     std::vector<int32_t> cu;     // packed cu_seqlens
     std::vector<int32_t> src;    // zigzag row -> packed token
-    // pass[ZZ_PASS_FWD..ZZ_PASS_BWD_DKV] are the ring passes; pass[kPassGathered]
-    // is the forward against every shard at once (one "step": its rank_off
-    // has cp+1 entries, its order_off 2).
-    zz::PassTables pass[4];
+    // pass[ZZ_PASS_FWD..ZZ_PASS_BWD_DKV] are the ring passes; pass[kPassGathered
+    // + ZZ_PASS_*] are the same walks against every shard at once (one
+    // "step": their rank_off has cp+1 entries, their order_off 2).
+    zz::PassTables pass[6];
     size_t off_src = 0;
     size_t ws_bytes = 0;
     std::vector<uint8_t> image;  // host image of the device workspace
@@ -72,7 +72,8 @@ zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, in
                      int32_t d, zz_dtype dt, int32_t bm, int32_t bn, zz_plan **out,
                      std::string *err);
 
-// Internal pass index of the gathered forward (not a public zz_pass value).
+// Internal pass index of the gathered walks: kPassGathered + ZZ_PASS_FWD /
+// _BWD_DQ / _BWD_DKV (not public zz_pass values).
 constexpr int kPassGathered = 3;
 
 // Device-side pointers into a bound plan's workspace.
@@ -113,6 +114,11 @@ hipError_t launch_debug_mask(const zz_plan *p, int pass, int rank, int step, uin
 // the normalised O and the LSE, no merge.
 hipError_t launch_fwd_gathered(const zz_plan *p, int rank, const void *q, const void *k, const void *v,
                                float *o, float *lse, hipStream_t st);
+// Backward of rank r against every shard (dq of its rows, dk/dv of its shard)
+// in one launch per kernel; writes (no accumulation across calls).
+hipError_t launch_bwd_gathered(const zz_plan *p, int rank, const void *q, const void *k, const void *v,
+                               const void *dout, const float *lse, const float *delta, float *dq, float *dk,
+                               float *dv, hipStream_t st);
 hipError_t launch_fwd_step(const zz_plan *p, int rank, int step, const void *q, const void *k,
                            const void *v, float *o, float *lse, int merge, hipStream_t st);
 // which: 1 = dK/dV kernel, 2 = dQ kernel, 3 = both.

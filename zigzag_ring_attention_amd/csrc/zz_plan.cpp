@@ -149,13 +149,15 @@ void build_pass(zz_plan *p, PassTables &t) {
     t.order_off[cp] = (int64_t)t.order.size();
 }
 
-// Gathered forward: every query item of rank r lists the visible tiles of
-// every shard, with key rows given in the global zigzag order (shard j's rows
-// start at j*T/cp), so the items carry shard 0 and one launch computes the
-// whole causal softmax of each row -- the all-gather alternative to the ring
-// (ring-attention-pytorch issue #20, "Zigzag attention support?": the
-// maintainer reads the scheme as gathering keys and values across ranks,
-// which GQA makes affordable, and plans to offer that gather as an option).
+// Gathered walks: every stationary item of rank r (its query rows for the
+// query-major walks, its key/value shard for the key-major one) lists the
+// visible tiles of every other rank's streamed rows, given in the global
+// zigzag order (rank j's rows start at j*T/cp), so the items carry a zero
+// base on the streamed side and one launch covers what the cp ring steps
+// cover -- the all-gather alternative to the ring (ring-attention-pytorch
+// issue #20, "Zigzag attention support?": the maintainer reads the scheme as
+// gathering keys and values across ranks, which GQA makes affordable, and
+// plans to offer that gather as an option).
 void build_gathered_pass(zz_plan *p, PassTables &t) {
     const int32_t cp = p->cp;
     const int64_t n = p->T / cp;
@@ -167,37 +169,49 @@ void build_gathered_pass(zz_plan *p, PassTables &t) {
     t.useful.assign((size_t)cp, 0);
     t.issued.assign((size_t)cp, 0);
     std::vector<int64_t> item_work;
+    std::vector<std::vector<std::vector<Chunk>>> ch((size_t)cp);
+    for (int32_t j = 0; j < cp; ++j) ch[(size_t)j] = local_chunks(p->cu, cp, j);
+    const int32_t sstep = t.key_major ? t.bn : t.bm;
+    const int32_t mstep = t.key_major ? t.bm : t.bn;
     for (int32_t r = 0; r < cp; ++r) {
         t.rank_off[(size_t)r] = (int64_t)t.items.size();
         const size_t first_item = t.items.size();
-        auto qch = local_chunks(p->cu, cp, r);
-        std::vector<std::vector<std::vector<Chunk>>> kch((size_t)cp);
-        for (int32_t j = 0; j < cp; ++j) kch[(size_t)j] = local_chunks(p->cu, cp, j);
         for (int32_t i = 0; i < p->nseq; ++i) {
-            for (const Chunk &a : qch[(size_t)i]) {
-                for (int32_t a0 = 0; a0 < a.len; a0 += t.bm) {
-                    const int32_t a1 = std::min(a0 + t.bm, a.len);
-                    WorkItem it{r, 0, a.start + a0, a.start + a1, (int32_t)t.tiles.size(), 0, 0, 0};
+            for (const Chunk &a : ch[(size_t)r][(size_t)i]) {
+                for (int32_t a0 = 0; a0 < a.len; a0 += sstep) {
+                    const int32_t a1 = std::min(a0 + sstep, a.len);
+                    // query-major: rank r's queries, keys at global rows (shard 0);
+                    // key-major: shard r's keys, queries at global rows (rank 0)
+                    WorkItem it{t.key_major ? 0 : r, t.key_major ? r : 0, a.start + a0, a.start + a1,
+                                (int32_t)t.tiles.size(), 0, 0, 0};
                     int64_t work = 0;
                     for (int32_t j = 0; j < cp; ++j) {
-                        for (const Chunk &b : kch[(size_t)j][(size_t)i]) {
-                            for (int32_t b0 = 0; b0 < b.len; b0 += t.bn) {
-                                const int32_t b1 = std::min(b0 + t.bn, b.len);
-                                int32_t delta;
-                                const int kind = classify(a.index, a0, a1, b.index, b0, b1, &delta);
+                        for (const Chunk &b : ch[(size_t)j][(size_t)i]) {
+                            for (int32_t b0 = 0; b0 < b.len; b0 += mstep) {
+                                const int32_t b1 = std::min(b0 + mstep, b.len);
+                                int32_t delta, kind, q0, q1, k0, k1;
+                                if (t.key_major) {
+                                    kind = classify(b.index, b0, b1, a.index, a0, a1, &delta);
+                                    q0 = b0; q1 = b1; k0 = a0; k1 = a1;
+                                } else {
+                                    kind = classify(a.index, a0, a1, b.index, b0, b1, &delta);
+                                    q0 = a0; q1 = a1; k0 = b0; k1 = b1;
+                                }
                                 if (!kind) continue;
                                 const int32_t g0 = (int32_t)(j * n + b.start + b0), g1 = (int32_t)(j * n + b.start + b1);
                                 t.tiles.push_back(TileRec{g0, g1, kind, delta});
-                                const int64_t area = (int64_t)(a1 - a0) * (b1 - b0);
+                                const int64_t area = (int64_t)(q1 - q0) * (k1 - k0);
                                 work += area;
                                 t.issued[(size_t)r] += area;
-                                t.useful[(size_t)r] += tile_pairs(kind, a0, a1, b0, b1, delta);
+                                t.useful[(size_t)r] += tile_pairs(kind, q0, q1, k0, k1, delta);
                             }
                         }
                     }
                     it.tend = (int32_t)t.tiles.size();
-                    t.items.push_back(it);   // every query row gets its O and LSE written
-                    item_work.push_back(work);
+                    if (it.tend > it.tbeg || t.keep_empty) {
+                        t.items.push_back(it);
+                        item_work.push_back(work);
+                    }
                 }
             }
         }
@@ -274,10 +288,13 @@ zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, in
     // LDS stage of the dK/dV kernel fits.
     dkv.bm = (dt == ZZ_F32 && d >= 64) ? 32 : 64;
     dkv.bn = 128; dkv.key_major = true; dkv.keep_empty = false;
-    PassTables &ga = p->pass[kPassGathered];
-    ga.bm = bm; ga.bn = bn; ga.key_major = false; ga.keep_empty = true;
-    for (int k = ZZ_PASS_FWD; k <= ZZ_PASS_BWD_DKV; ++k) build_pass(p, p->pass[k]);
-    build_gathered_pass(p, ga);
+    for (int k = ZZ_PASS_FWD; k <= ZZ_PASS_BWD_DKV; ++k) {
+        PassTables &g = p->pass[kPassGathered + k];
+        const PassTables &r = p->pass[k];
+        g.bm = r.bm; g.bn = r.bn; g.key_major = r.key_major; g.keep_empty = r.keep_empty;
+        build_pass(p, p->pass[k]);
+        build_gathered_pass(p, g);
+    }
 
     // Workspace image: zigzag map, then items / tiles / order of each pass.
     size_t off = 0;
