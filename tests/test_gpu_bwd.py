@@ -35,6 +35,7 @@ def check_grads(case, tol):
     ((8, 24, 16), 4, 4, 2, 64),
     ((40, 24), 1, 2, 1, 32),
     ((200, 56), 2, 4, 2, 32),
+    ((64, 192), 2, 2, 1, 128),       # fp32 head_dim 128: 32-row dK/dV query tiles, 32-key dQ tiles
 ])
 def test_backward_fp32(lengths, cp, hq, hkv, d):
     case = Case(lengths, cp, hq, hkv, d, "f32", 21, with_do=True)
@@ -45,6 +46,8 @@ def test_backward_fp32(lengths, cp, hq, hkv, d):
     ((128, 256, 64), 2, 4, 2, 128, 1.0),
     ((16, 48, 528, 8), 4, 8, 1, 128, 1.0),
     ((512,), 4, 8, 1, 128, 4.0),
+    ((96, 160, 8), 2, 4, 2, 64, 1.0),    # head_dim 64
+    ((40, 24, 200), 2, 2, 2, 32, 2.0),   # head_dim 32, MHA
 ])
 def test_backward_bf16(lengths, cp, hq, hkv, d, q_scale):
     case = Case(lengths, cp, hq, hkv, d, "bf16", 23, with_do=True, q_scale=q_scale)

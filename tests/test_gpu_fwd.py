@@ -137,6 +137,8 @@ def test_forward_c1_fp32_full():
     ((40, 24), 1, 2, 2, 64, "f32", 1.0),               # one rank
     ((40, 24), 2, 2, 2, 32, "bf16", 1.0),
     ((512,), 4, 2, 2, 64, "f32", 4.0),
+    ((64, 192), 2, 2, 1, 128, "f32", 1.0),            # fp32 head_dim 128 (128 KB of LDS)
+    ((200, 56), 2, 4, 4, 64, "bf16", 1.0),            # bf16 head_dim 64, MHA
 ])
 def test_forward_small_full(lengths, cp, hq, hkv, d, dtype, q_scale):
     case = Case(lengths, cp, hq, hkv, d, dtype, 9, q_scale=q_scale)

@@ -99,6 +99,7 @@ def gathered_grads(case):
     ((200, 56), 2, 4, 2, 32, "f32"),
     ((128, 256, 64), 2, 4, 2, 128, "bf16"),
     ((16, 48, 528, 8), 4, 8, 1, 128, "bf16"),
+    ((96, 160, 8), 2, 4, 2, 64, "bf16"),
 ])
 def test_gathered_backward_matches_oracle(lengths, cp, hq, hkv, d, dtype):
     case = Case(lengths, cp, hq, hkv, d, dtype, 37, with_do=True)
