@@ -257,10 +257,18 @@ def main():
     achieved = per_launch[dom] / (ks[dom]["mean_ms"] * 1e-3) / 1e12
     # HBM bytes per launch of the dominant kernel from the committed counter
     # summary of this workload (None once the kernel sources have changed).
+    # Clock and matrix-unit busy fraction of the three kernels under this
+    # load, from the committed counter summary (None once sources changed).
     traffic = None
+    util = None
     if w.name == "c5":
         from zigzag_ring_attention_amd import profiling
         traffic = profiling.read_traffic(os.path.join(ROOT, "profiles", "c5_hbm_traffic.txt"), dom + "_kernel")
+        u = profiling.read_util(os.path.join(ROOT, "profiles", "c5_mfma_utilization.md"))
+        if u:
+            util = {"source": "profiles/c5_mfma_utilization.md (rocprofv3 --pmc)"}
+            for name, (ghz, busy) in u.items():
+                util[name] = {"clock_ghz": ghz, "mfma_busy": busy}
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     fwd_ms = ks["fwd_gathered" if args.gathered else "fwd_step"]["total_ms"] / args.steps
     if not backward:
@@ -335,6 +343,7 @@ def main():
             "frac": round(achieved / peak, 4),
             "traffic": traffic,
         },
+        "mfma_util": util,
         "permute": permute,
         "balance": balance,
         "cpu_baseline": cpu,

@@ -122,6 +122,7 @@ def util_markdown(path: str, command: str) -> str:
         dtype[k] = "bf16" if "DF16b" in r["Kernel_Name"] else "f32"
     out = ["# MFMA utilisation and clock, rocprofv3 --pmc", "",
            "Command: `%s`" % command, "",
+           "kernel_sources_sha256 %s" % sources_hash(), "",
            "Per dispatch (mean): executed matrix work = SQ_INSTS_MFMA x FLOP per instruction; "
            "busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x %d SIMDs); clock = GRBM_GUI_ACTIVE / %d XCDs / time. "
            "The clock-adjusted peak is %d FLOP/clk/SIMD x %d SIMDs x clock (2.5166 PFLOP/s at %.1f GHz)."
@@ -143,6 +144,22 @@ def util_markdown(path: str, command: str) -> str:
             k, len(ds), t * 1e3, flop / 1e12, flop / t / 1e12, cyc / t / 1e9, busy / (cyc * SIMDS),
             flop / t / nominal))
     return "\n".join(out) + "\n"
+
+
+def read_util(path: str):
+    """{kernel: (clock GHz, MFMA busy fraction)} from a utilisation summary,
+    or None if the file is missing or the kernel sources changed since it was
+    taken."""
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^kernel_sources_sha256 (\S+)", text, re.M)
+    if not m or m.group(1) != sources_hash():
+        return None
+    out = {}
+    for row in re.finditer(r"^\| (\w+)_kernel \| \d+ \| [\d.]+ \| [\d.]+ \| [\d.]+ \| ([\d.]+) \| ([\d.]+) \|", text, re.M):
+        out[row.group(1)] = (float(row.group(2)), float(row.group(3)))
+    return out or None
 
 
 def read_traffic(path: str, kernel: str):
