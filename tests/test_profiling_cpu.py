@@ -79,3 +79,22 @@ def test_stale_summaries_are_withheld(tmp_path):
     u.write_text("kernel_sources_sha256 %s\n\n%s" % (h, row))
     assert profiling.read_util(str(u)) == {"fwd_step": (1.817, 0.546)}
     assert profiling.read_util(str(tmp_path / "missing.md")) is None
+
+
+def test_issue_mix_ratios(tmp_path):
+    name = "void zz::bwd_dq_kernel<bf16, 128>(zz::BwdArgs)"
+    a = {"SQ_INSTS_VALU": 500.0, "SQ_INSTS_MFMA": 100.0, "SQ_INSTS_LDS": 150.0, "SQ_INSTS_SALU": 50.0,
+         "SQ_INSTS_VMEM_RD": 10.0, "SQ_WAVES": 4.0, "SQ_WAVE_CYCLES": 1000.0, "SQ_BUSY_CYCLES": 300.0}
+    b = {"SQ_VALU_MFMA_BUSY_CYCLES": 3200.0 * profiling.SIMDS / 1e4, "SQ_VALU_MFMA_COEXEC_CYCLES": 80.0,
+         "SQ_ACTIVE_INST_VALU": 1.0, "SQ_ACTIVE_INST_LDS": 1.0, "SQ_WAIT_INST_LDS": 50.0, "SQ_WAIT_ANY": 250.0,
+         "SQ_INSTS_VALU_TRANS_F32": 60.0, "GRBM_GUI_ACTIVE": 6400.0 * profiling.XCDS / 1e4 * 1e4}
+    for fn, counters in (("a.csv", a), ("b.csv", b)):
+        write_csv(tmp_path / fn, [dict(Dispatch_Id=1, Kernel_Name=name, Counter_Name=c, Counter_Value=v)
+                                  for c, v in counters.items()])
+    text = profiling.issue_markdown([str(tmp_path / "a.csv"), str(tmp_path / "b.csv")], "cmd")
+    row = [l for l in text.splitlines() if l.startswith("| bwd_dq_kernel")][0]
+    cells = [float(x) for x in row.strip("|").split("|")[1:]]
+    # (500-100)/100, 60/100, 150/100, 50/100, 10/100, busy 3200*S/1e4 / (6400 * S), co-exec 80/busy, 250/1000, 50/1000
+    busy = b["SQ_VALU_MFMA_BUSY_CYCLES"]
+    want = [4.0, 0.6, 1.5, 0.5, 0.1, busy / (6400.0 * profiling.SIMDS), 80.0 / busy, 0.25, 0.05]
+    assert cells == pytest.approx(want, abs=1e-3)

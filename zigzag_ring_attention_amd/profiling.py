@@ -146,6 +146,55 @@ def util_markdown(path: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
+ISSUE_COUNTERS = (
+    ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM_RD", "SQ_WAVES",
+     "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES"),
+    ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+     "SQ_WAIT_INST_LDS", "SQ_WAIT_ANY", "SQ_INSTS_VALU_TRANS_F32", "GRBM_GUI_ACTIVE"),
+)
+
+
+def issue_markdown(paths, command: str) -> str:
+    """Instruction mix and issue/wait cycles per libzz kernel from the two
+    `--pmc` passes of ISSUE_COUNTERS (one CSV each).  SQ_INSTS_VALU includes
+    the MFMA instructions; the SQ_*_CYCLES and SQ_ACTIVE_/SQ_WAIT_ counters
+    are summed over waves in units of 4 clocks."""
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    nd = collections.defaultdict(set)
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            k = short_name(r["Kernel_Name"])
+            if k not in ("fwd_step_kernel", "bwd_dkv_kernel", "bwd_dq_kernel"):
+                continue
+            per[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            nd[(k, path)].add(r["Dispatch_Id"])
+    out = ["# Instruction mix and issue cycles, rocprofv3 --pmc (two passes)", "",
+           "Command: `%s`" % command, "",
+           "kernel_sources_sha256 %s" % sources_hash(), "",
+           "Per MFMA instruction: vector (non-MFMA), transcendental, LDS, scalar and vector-memory instructions. "
+           "Co-exec = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (share of matrix-busy cycles with a "
+           "vector instruction in flight beside it); MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE/%d x %d "
+           "SIMDs); wait any / LDS wait = share of wave-cycles waiting on anything / on LDS results." % (XCDS, SIMDS), "",
+           "| kernel | VALU/MFMA | trans/MFMA | LDS/MFMA | SALU/MFMA | VMEM/MFMA | MFMA busy | co-exec | wait any | LDS wait |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
+    for k in ("fwd_step_kernel", "bwd_dkv_kernel", "bwd_dq_kernel"):
+        if k not in per:
+            continue
+        c = per[k]
+        mf = c["SQ_INSTS_MFMA"]
+        if mf <= 0:
+            continue
+        cyc = c["GRBM_GUI_ACTIVE"] / XCDS
+        out.append("| %s | %.2f | %.2f | %.2f | %.2f | %.3f | %.3f | %.3f | %.3f | %.3f |" % (
+            k, (c["SQ_INSTS_VALU"] - mf) / mf, c["SQ_INSTS_VALU_TRANS_F32"] / mf, c["SQ_INSTS_LDS"] / mf,
+            c["SQ_INSTS_SALU"] / mf, c["SQ_INSTS_VMEM_RD"] / mf,
+            c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * SIMDS) if cyc else float("nan"),
+            c["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(1.0, c["SQ_VALU_MFMA_BUSY_CYCLES"]),
+            c["SQ_WAIT_ANY"] / max(1.0, c["SQ_WAVE_CYCLES"]),
+            c["SQ_WAIT_INST_LDS"] / max(1.0, c["SQ_WAVE_CYCLES"])))
+    return "\n".join(out) + "\n"
+
+
 def read_util(path: str):
     """{kernel: (clock GHz, MFMA busy fraction)} from a utilisation summary,
     or None if the file is missing or the kernel sources changed since it was
@@ -180,6 +229,8 @@ if __name__ == "__main__":
         sys.stdout.write(stats_markdown(sys.argv[2], " ".join(sys.argv[3:])))
     elif sys.argv[1] == "util":
         sys.stdout.write(util_markdown(sys.argv[2], " ".join(sys.argv[3:])))
+    elif sys.argv[1] == "issue":
+        sys.stdout.write(issue_markdown(sys.argv[2:4], " ".join(sys.argv[4:])))
     elif sys.argv[1] == "traffic":
         # copy size of the first permute of a bench step: Q of the workload
         # (c5 unless "--workload cN" follows the two files)
@@ -193,4 +244,4 @@ if __name__ == "__main__":
         copy_bytes = float(w.total * w.hq * w.d * (2 if w.dtype == "bf16" else 4))
         sys.stdout.write(traffic_text(sys.argv[2], sys.argv[3], " ".join(rest), copy_bytes))
     else:
-        raise SystemExit("usage: profiling.py stats|traffic ...")
+        raise SystemExit("usage: profiling.py stats|util|issue|traffic ...")
