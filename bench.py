@@ -128,6 +128,9 @@ def main():
     ap.add_argument("--no-balance", action="store_true")
     ap.add_argument("--with-backward", action="store_true",
                     help="also time the backward on a forward-only workload (synthetic dO)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one step captured in a HIP graph (one eager step gives the kernel "
+                         "times); replays are checked bit for bit against the eager step first")
     ap.add_argument("--gathered", action="store_true",
                     help="the all-gather form: forward and backward as one launch (per kernel) against "
                          "all shards, no step partials, merges or accumulation")
@@ -232,10 +235,40 @@ def main():
         log("bench: warmup step %d done" % i)
 
     tm = Timers()
+    graph = None
+    if args.graph:
+        # kernel times from one eager step, then the step captured once and
+        # replayed; the library's calls launch on torch's current stream, which
+        # is the capture stream inside the graph context
+        step(tm)
+        torch.cuda.synchronize()
+        outs = [o_zz] + (list(grads) if backward else [])
+        want = [x.clone() for x in outs]
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(None)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step(None)
+        for rep in range(2):
+            for x in outs:
+                x.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            for x, y in zip(outs, want):
+                if not torch.equal(x, y):
+                    raise SystemExit("graph replay %d differs from the eager step" % rep)
+        log("bench: graph captured, replays match the eager step")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(tm)
+        if graph is not None:
+            graph.replay()
+        else:
+            step(tm)
         if i + 1 < args.steps:
             torch.cuda.synchronize()
             log("bench: timed step %d done" % i)
@@ -270,13 +303,14 @@ def main():
             for name, (ghz, busy) in u.items():
                 util[name] = {"clock_ghz": ghz, "mfma_busy": busy}
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
-    fwd_ms = ks["fwd_gathered" if args.gathered else "fwd_step"]["total_ms"] / args.steps
+    timed_steps = 1 if args.graph else args.steps   # steps the kernel timers saw
+    fwd_ms = ks["fwd_gathered" if args.gathered else "fwd_step"]["total_ms"] / timed_steps
     if not backward:
         bwd_ms = 0.0
     elif args.gathered:
-        bwd_ms = ks["bwd_gathered"]["total_ms"] / args.steps
+        bwd_ms = ks["bwd_gathered"]["total_ms"] / timed_steps
     else:
-        bwd_ms = (ks["bwd_dkv"]["total_ms"] + ks["bwd_dq"]["total_ms"]) / args.steps
+        bwd_ms = (ks["bwd_dkv"]["total_ms"] + ks["bwd_dq"]["total_ms"]) / timed_steps
 
     balance = None
     if not args.no_balance and not args.gathered:
@@ -324,7 +358,8 @@ def main():
             "workload": "%s: %s, %d tokens, lengths %s, GQA %d/%d, head_dim %d, simulated CP=%d zigzag, %s"
                         % (w.name, w.dtype, T, ("%d sequences" % (len(cu) - 1)) if len(cu) > 2 else "one causal sequence",
                            hq, hkv, d, cp, ("forward + backward" if backward else "forward")
-                           + (", all-gather K/V form" if args.gathered else "")),
+                           + (", all-gather K/V form" if args.gathered else "")
+                           + (", step replayed from a HIP graph" if args.graph else "")),
             "tokens": T, "heads_q": hq, "heads_kv": hkv, "head_dim": d, "cp": cp,
             "parallelism": "cp%d simulated on 1 GPU" % cp,
         },
