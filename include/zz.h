@@ -136,6 +136,22 @@ zz_status zz_plan_tiles(const zz_plan *plan, zz_pass pass, int32_t rank, int32_t
                         int32_t *out, int64_t cap, int64_t *n);
 
 /*
+ * Tiles the all-gather form walks (zz_varlen_gathered_fwd / _bwd; the
+ * gather of keys and values across ranks is the reading of zigzag attention
+ * in ring-attention-pytorch issue #20, "Zigzag attention support?") for one
+ * stationary owner: the query rows of rank `owner` (ZZ_PASS_FWD,
+ * ZZ_PASS_BWD_DQ) or the key rows of shard `owner` (ZZ_PASS_BWD_DKV),
+ * against the rows of every shard or rank.  Same layout, order, kinds and
+ * capacity rule as zz_plan_tiles, but every row index is a GLOBAL zigzag row
+ * (rank or shard j's rows start at j*T/cp).  Each list is the union over the
+ * ring steps of the corresponding zz_plan_tiles lists, shifted to global rows.
+ * Errors: ZZ_ERR_ARG for a null plan, bad pass, owner outside [0, cp) or a
+ * null output; ZZ_ERR_WORKSPACE as above.
+ */
+zz_status zz_plan_gathered_tiles(const zz_plan *plan, zz_pass pass, int32_t owner,
+                                 int32_t *out, int64_t cap, int64_t *n);
+
+/*
  * Pair counts for rank/step (either may be ZZ_ALL_RANKS / ZZ_ALL_STEPS):
  * useful = visible (query, key) pairs per head; issued = pairs covered by the
  * pass's visited tiles (what the MFMA units process).

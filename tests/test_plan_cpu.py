@@ -169,3 +169,28 @@ def test_contiguous_split_would_be_unbalanced():
         p = zz.Plan([0, L], cp, 1, 1, 32, "f32")
         zzw = [p.pair_counts(r)[0] for r in range(cp)]
         assert max(zzw) == min(zzw)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_gathered_tiles_are_the_union_of_ring_steps(name):
+    """The all-gather walks list exactly the tiles of the ring steps (pinned
+    above against the oracle), moved to global zigzag rows: rank r's queries
+    against every shard j = (r - s) mod cp, and shard j's keys against every
+    rank r = (j + s) mod cp."""
+    w = synthetic.WORKLOADS[name]
+    cu = synthetic.cu_seqlens_for(w)
+    plan = zz.Plan(cu, w.cp, w.hq, w.hkv, w.d, w.dtype)
+    n = plan.total // w.cp
+    for pass_ in (zz.PASS_FWD, zz.PASS_BWD_DQ, zz.PASS_BWD_DKV):
+        for owner in range(w.cp):
+            parts = []
+            for s in range(w.cp):
+                r, j = ((owner + s) % w.cp, owner) if pass_ == zz.PASS_BWD_DKV else (owner, (owner - s) % w.cp)
+                t = plan.tiles(r, s, pass_).astype(np.int64)
+                t[:, 0:2] += r * n
+                t[:, 2:4] += j * n
+                parts.append(t)
+            want = np.concatenate(parts)
+            want = want[np.lexsort((want[:, 2], want[:, 0]))]
+            got = plan.gathered_tiles(owner, pass_)
+            assert np.array_equal(got, want), (pass_, owner)

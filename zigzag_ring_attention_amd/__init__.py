@@ -66,6 +66,7 @@ def lib():
         "zz_plan_zigzag_dst": ([P, P], i32),
         "zz_plan_tile_shape": ([P, i32, P, P], i32),
         "zz_plan_tiles": ([P, i32, i32, i32, P, i64, P], i32),
+        "zz_plan_gathered_tiles": ([P, i32, i32, P, i64, P], i32),
         "zz_plan_pair_counts": ([P, i32, i32, i32, P, P], i32),
         "zz_zigzag_permute": ([P, P, P, i64, P], i32),
         "zz_zigzag_unpermute": ([P, P, P, i64, P], i32),
@@ -191,6 +192,19 @@ class Plan:
         out = np.empty((max(n.value, 1), 5), dtype=np.int32)
         _check(L.zz_plan_tiles(self._h, pass_, rank, step, out.ctypes.data_as(ctypes.c_void_p),
                                n.value, ctypes.byref(n)), "zz_plan_tiles")
+        return out[: n.value]
+
+    def gathered_tiles(self, owner: int, pass_: int = PASS_FWD) -> np.ndarray:
+        """Tiles of the all-gather form for rank (or, for the dK/dV pass,
+        shard) `owner`: [n, 5] (q0, q1, k0, k1, kind) in global zigzag rows."""
+        L = lib()
+        n = ctypes.c_int64()
+        rc = L.zz_plan_gathered_tiles(self._h, pass_, owner, None, 0, ctypes.byref(n))
+        if rc not in (0, 5):
+            _check(rc, "zz_plan_gathered_tiles")
+        out = np.empty((max(n.value, 1), 5), dtype=np.int32)
+        _check(L.zz_plan_gathered_tiles(self._h, pass_, owner, out.ctypes.data_as(ctypes.c_void_p),
+                                        n.value, ctypes.byref(n)), "zz_plan_gathered_tiles")
         return out[: n.value]
 
     def pair_counts(self, rank: int = ALL_RANKS, step: int = ALL_STEPS, pass_: int = PASS_FWD):

@@ -55,6 +55,7 @@ zz_status hip_status(hipError_t e, const char *what) {
 
 extern "C" {
 
+
 const char *zz_status_str(zz_status s) {
     switch (s) {
         case ZZ_OK: return "ok";
@@ -133,22 +134,21 @@ zz_status zz_plan_tile_shape(const zz_plan *p, zz_pass pass, int32_t *bm, int32_
     return ZZ_OK;
 }
 
-zz_status zz_plan_tiles(const zz_plan *p, zz_pass pass, int32_t rank, int32_t step, int32_t *out,
-                        int64_t cap, int64_t *n) {
-    ZZ_TRY(check_plan(p, false));
-    if (pass < ZZ_PASS_FWD || pass > ZZ_PASS_BWD_DKV) return fail(ZZ_ERR_ARG, "bad pass");
-    ZZ_TRY(check_rank_step(p, rank, step, false));
-    if (!n || (cap > 0 && !out)) return fail(ZZ_ERR_ARG, "null output");
-    const zz::PassTables &t = p->pass[pass];
+// Tiles of items [b, e) of a pass as (q0, q1, k0, k1, kind), the stationary
+// rows shifted by `stat_base` and the streamed rows by `stream_base`, sorted
+// by (q0, k0) and copied out under the capacity rule of zz_plan_tiles.
+static zz_status emit_tiles(const zz::PassTables &t, int64_t b, int64_t e, int64_t stat_base, int64_t stream_base,
+                     int32_t *out, int64_t cap, int64_t *n) {
     struct Q { int32_t q0, q1, k0, k1, kind; };
     std::vector<Q> v;
-    const int64_t b = t.rank_off[(size_t)step * p->cp + rank], e = t.rank_off[(size_t)step * p->cp + rank + 1];
     for (int64_t u = b; u < e; ++u) {
         const zz::WorkItem &it = t.items[(size_t)u];
+        const int32_t s0 = (int32_t)(stat_base + it.a0), s1 = (int32_t)(stat_base + it.a1);
         for (int32_t x = it.tbeg; x < it.tend; ++x) {
             const zz::TileRec &tr = t.tiles[(size_t)x];
-            if (t.key_major) v.push_back(Q{tr.b0, tr.b1, it.a0, it.a1, tr.kind});
-            else v.push_back(Q{it.a0, it.a1, tr.b0, tr.b1, tr.kind});
+            const int32_t m0 = (int32_t)(stream_base + tr.b0), m1 = (int32_t)(stream_base + tr.b1);
+            if (t.key_major) v.push_back(Q{m0, m1, s0, s1, tr.kind});
+            else v.push_back(Q{s0, s1, m0, m1, tr.kind});
         }
     }
     std::sort(v.begin(), v.end(), [](const Q &a, const Q &c) {
@@ -162,6 +162,29 @@ zz_status zz_plan_tiles(const zz_plan *p, zz_pass pass, int32_t rank, int32_t st
     }
     if ((int64_t)v.size() > cap) return fail(ZZ_ERR_WORKSPACE, "tile output capacity too small");
     return ZZ_OK;
+}
+
+zz_status zz_plan_tiles(const zz_plan *p, zz_pass pass, int32_t rank, int32_t step, int32_t *out,
+                        int64_t cap, int64_t *n) {
+    ZZ_TRY(check_plan(p, false));
+    if (pass < ZZ_PASS_FWD || pass > ZZ_PASS_BWD_DKV) return fail(ZZ_ERR_ARG, "bad pass");
+    ZZ_TRY(check_rank_step(p, rank, step, false));
+    if (!n || (cap > 0 && !out)) return fail(ZZ_ERR_ARG, "null output");
+    const zz::PassTables &t = p->pass[pass];
+    const int64_t b = t.rank_off[(size_t)step * p->cp + rank], e = t.rank_off[(size_t)step * p->cp + rank + 1];
+    return emit_tiles(t, b, e, 0, 0, out, cap, n);
+}
+
+zz_status zz_plan_gathered_tiles(const zz_plan *p, zz_pass pass, int32_t owner, int32_t *out, int64_t cap,
+                                 int64_t *n) {
+    ZZ_TRY(check_plan(p, false));
+    if (pass < ZZ_PASS_FWD || pass > ZZ_PASS_BWD_DKV) return fail(ZZ_ERR_ARG, "bad pass");
+    if (owner < 0 || owner >= p->cp) return fail(ZZ_ERR_ARG, "owner out of range");
+    if (!n || (cap > 0 && !out)) return fail(ZZ_ERR_ARG, "null output");
+    const zz::PassTables &t = p->pass[zz::kPassGathered + pass];
+    // stationary rows are local to the owner; streamed rows are already global
+    return emit_tiles(t, t.rank_off[(size_t)owner], t.rank_off[(size_t)owner + 1], (int64_t)owner * (p->T / p->cp),
+                      0, out, cap, n);
 }
 
 zz_status zz_plan_pair_counts(const zz_plan *p, zz_pass pass, int32_t rank, int32_t step,
