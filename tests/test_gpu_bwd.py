@@ -36,6 +36,8 @@ def check_grads(case, tol):
     ((40, 24), 1, 2, 1, 32),
     ((200, 56), 2, 4, 2, 32),
     ((64, 192), 2, 2, 1, 128),       # fp32 head_dim 128: 32-row dK/dV query tiles, 32-key dQ tiles
+    ((36, 12, 60, 96), 3, 4, 2, 64),  # CP not a power of two
+    ((64, 128, 320), 32, 2, 1, 32),   # CP 32
 ])
 def test_backward_fp32(lengths, cp, hq, hkv, d):
     case = Case(lengths, cp, hq, hkv, d, "f32", 21, with_do=True)

@@ -139,6 +139,9 @@ def test_forward_c1_fp32_full():
     ((512,), 4, 2, 2, 64, "f32", 4.0),
     ((64, 192), 2, 2, 1, 128, "f32", 1.0),            # fp32 head_dim 128 (128 KB of LDS)
     ((200, 56), 2, 4, 4, 64, "bf16", 1.0),            # bf16 head_dim 64, MHA
+    ((36, 12, 60, 96), 3, 4, 2, 64, "f32", 1.0),      # CP not a power of two
+    ((96, 36, 150), 3, 4, 2, 128, "bf16", 1.0),
+    ((64, 128, 320), 32, 2, 1, 32, "f32", 1.0),       # CP 32: one- and two-row chunks, 1024 rank-steps
 ])
 def test_forward_small_full(lengths, cp, hq, hkv, d, dtype, q_scale):
     case = Case(lengths, cp, hq, hkv, d, dtype, 9, q_scale=q_scale)
