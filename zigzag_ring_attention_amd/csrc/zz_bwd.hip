@@ -11,59 +11,16 @@
 //    query tile (up to 64 rows, staged in LDS with its LSE and delta), forming
 //    S and dP with the keys in the lane dimension, so that P and dS are
 //    directly the operands of dV^T += dO^T P and dK^T += Q^T dS.
-//  * dq (query-major): like the forward step, S^T and dP^T with the queries in
-//    the lane dimension, then dQ^T += K^T dS^T.
+//  * dq (query-major, zz_bwd_dq.hip): like the forward step, S^T and dP^T
+//    with the queries in the lane dimension, then dQ^T += K^T dS^T.
 // Fully masked tiles are never visited (tile lists from the planner).
 
 #include <type_traits>
 
-#include "zz_mfma.h"
-
-// Waves per SIMD each kernel is compiled for (register budget 512 / waves).
-#ifndef ZZ_DQ_WAVES
-#define ZZ_DQ_WAVES 2
-#endif
+#include "zz_bwd.h"
 
 namespace zz {
 namespace {
-
-constexpr int kThreads = 256;
-// s_waitcnt immediate that waits for vmcnt = 0 only (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8; the others at their maximum).
-constexpr int kWaitVmcnt0 = 0x0F70;
-constexpr float kLog2e = 1.4426950408889634f;
-
-struct BwdArgs {
-    const void *q, *k, *v, *dout;
-    const float *lse, *delta;
-    float *dq, *dk, *dv;
-    const WorkItem *items;
-    const int32_t *order;
-    const TileRec *tiles;
-    int64_t T;
-    int32_t n, hq, hkv;
-    float scale, scale_log2;
-    int32_t accumulate;
-    int32_t nitems;   // work items in this launch
-};
-
-// Read-add-write of a lane's column of a transposed accumulator (C layout:
-// register i of block b is element 32*b + c_row(i, l/32) of the row).
-template <int NB>
-__device__ __forceinline__ void add_row(float *row, const f32x16 (&acc)[NB], float mul, int hh, bool accumulate) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-            float4 *dst = reinterpret_cast<float4 *>(row + 32 * b + c_row(4 * i4, hh));
-            float4 o = accumulate ? *dst : float4{0.f, 0.f, 0.f, 0.f};
-            o.x += acc[b][4 * i4 + 0] * mul;
-            o.y += acc[b][4 * i4 + 1] * mul;
-            o.z += acc[b][4 * i4 + 2] * mul;
-            o.w += acc[b][4 * i4 + 3] * mul;
-            *dst = o;
-        }
-}
 
 // ---------------------------------------------------------------- dK, dV
 
@@ -298,112 +255,6 @@ bwd_dkv_kernel(BwdArgs a) {
     else add_row<NB>(a.dk + (krow * a.hkv + kvh) * D, acc, a.scale, hh, a.accumulate != 0);
 }
 
-// ---------------------------------------------------------------- dQ
-
-// Keys per streamed tile (must match the planner's dQ tile): halved for fp32
-// with D >= 64 so the double-buffered LDS stage fits.
-template <typename T, int D> constexpr int k_tile() { return (sizeof(T) == 4 && D >= 64) ? 32 : 64; }
-constexpr int kDqThreads = 512;    // eight waves own 32 query rows each
-
-// Query-major: a workgroup owns up to 256 query rows of one head (eight
-// waves of 32) and walks the item's key tiles, with the K and V tiles copied
-// global -> LDS by the memory unit into double buffers (K^T is read from the
-// K tile by LDS transpose reads).
-template <typename T, int D>
-__global__ void __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(ZZ_DQ_WAVES)))
-bwd_dq_kernel(BwdArgs a) {
-    using M = Mfma<T, D>;
-    constexpr int kKT = k_tile<T, D>();
-    constexpr int NW = kDqThreads / 64;
-    using DmaRows = Dma<kKT, M::W, NW>;
-    constexpr int NB = D / 32;
-    // K (S^T = K Q^T, and read transposed for dQ^T += K^T dS^T) and V
-    // (dP^T = V dO^T), row-major.
-    __shared__ __attribute__((aligned(16))) T Ks[2][kKT * D];
-    __shared__ __attribute__((aligned(16))) T Vs[2][kKT * D];
-
-    const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    int item_ix, head;
-    block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
-    const int kvh = head / (a.hq / a.hkv);
-    const WorkItem it = load_const(a.items, a.order ? load_const(a.order, item_ix) : item_ix);
-    const int nq = it.a1 - it.a0;
-    const int qq = wave * 32 + (lane & 31);
-    const bool row_ok = qq < nq;
-    const bool wave_on = wave * 32 < nq;
-    const int64_t zrow = (int64_t)it.rank * a.n + it.a0 + qq;
-    const T *k = static_cast<const T *>(a.k);
-    const T *v = static_cast<const T *>(a.v);
-
-    typename M::Op qop[M::KS], dop[M::KS];
-    float lse2 = 0.0f, dlt = 0.0f;
-    if (row_ok) {
-        M::load_row_op(qop, static_cast<const T *>(a.q) + (zrow * a.hq + head) * D, hh);
-        M::load_row_op(dop, static_cast<const T *>(a.dout) + (zrow * a.hq + head) * D, hh);
-        lse2 = a.lse[(int64_t)head * a.T + zrow] * kLog2e;
-        dlt = a.delta[(int64_t)head * a.T + zrow];
-    } else {
-        M::zero_op(qop);
-        M::zero_op(dop);
-    }
-    f32x16 acc[NB];
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
-    const int64_t kv_row0 = (int64_t)it.shard * a.n;
-
-    const DmaRows dma((uint32_t)(a.hkv * D * sizeof(T)), wave, lane);
-    TileWindow win(a.tiles, it.tbeg, it.tend - it.tbeg, lane);
-    auto copy_tile = [&](const TileRec &tn, T *ks, T *vs) __attribute__((always_inline)) {
-        const int nk = tn.b1 - tn.b0;
-        dma.issue(tile_base<T, D>(k, kv_row0 + tn.b0, a.hkv, kvh), nk, ks);
-        dma.issue(tile_base<T, D>(v, kv_row0 + tn.b0, a.hkv, kvh), nk, vs);
-    };
-    // One tile, as in the forward step: the copy of tile t+1 overlaps this
-    // tile's work; constant buffers (loop unrolled by two).
-    TileRec cur = win.get(0);
-    auto tile_step = [&](int t, const T *ks, const T *vs, T *ks_next, T *vs_next) __attribute__((always_inline)) {
-        const TileRec tr = cur;
-        const int nk = tr.b1 - tr.b0;
-        cur = win.get(min(t + 1, it.tend - 1) - it.tbeg);
-        copy_tile(cur, ks_next, vs_next);
-        if (wave_on) {
-#pragma unroll
-            for (int kb = 0; kb < kKT / 32; ++kb) {
-                f32x16 s, dp;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
-                M::gemm_rows_lds_pair(s, ks, qop, dp, vs, dop, kb * 32 + (lane & 31), hh);
-                // mask (partial and ragged tiles only): key kk is kept iff kk < nk
-                // and, in a partial tile, kk <= qq + delta; rows of queries past
-                // the item are never written
-                if (tr.kind != ZZ_TILE_FULL || nk < kKT)
-                    mask_rows_above(s, (tr.kind == ZZ_TILE_FULL ? nk - 1 : min(nk - 1, qq + tr.delta)) - kb * 32 -
-                                           4 * hh);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
-                    dp[i] = p * (dp[i] - dlt);
-                }
-                M::gemm_t_c(acc, ks, kb * 32, dp, lane);
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this wave's copies of tile t+1 have landed
-        __syncthreads();
-    };
-    copy_tile(cur, Ks[0], Vs[0]);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // the query-side operands and tile 0 have landed
-    __syncthreads();
-    for (int t = it.tbeg; t < it.tend; t += 2) {
-        tile_step(t, Ks[0], Vs[0], Ks[1], Vs[1]);
-        if (t + 1 < it.tend) tile_step(t + 1, Ks[1], Vs[1], Ks[0], Vs[0]);
-    }
-    if (!row_ok) return;
-    add_row<NB>(a.dq + (zrow * a.hq + head) * D, acc, a.scale, hh, a.accumulate != 0);
-}
-
 template <typename T, int D>
 hipError_t launch_t(const zz_plan *p, int base, int rank, int step, BwdArgs a, int which, hipStream_t st) {
     const int pkv = base + ZZ_PASS_BWD_DKV, pq = base + ZZ_PASS_BWD_DQ;
@@ -414,12 +265,8 @@ hipError_t launch_t(const zz_plan *p, int base, int rank, int step, BwdArgs a, i
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const Launch Lq = launch_items(p, pq, rank, step);
-    if ((which & 2) && Lq.n > 0) {
-        a.items = Lq.items; a.order = Lq.order; a.tiles = dev_tiles(p, pq); a.nitems = Lq.n;
-        hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(Lq.n * p->hq), dim3(kDqThreads), 0, st, a);
-    }
-    return hipGetLastError();
+    if (which & 2) return launch_dq(p, pq, rank, step, a, st);
+    return hipSuccess;
 }
 
 hipError_t launch_bwd_pass(const zz_plan *p, int base, int rank, int step, const void *q, const void *k,

@@ -27,7 +27,8 @@ import re
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = ["zz_fwd.hip", "zz_bwd.hip", "zz_mfma.h", "zz_device.h", "zz_util.hip", "zz_internal.h"]
+KERNEL_SOURCES = ["zz_fwd.hip", "zz_bwd.hip", "zz_bwd_dq.hip", "zz_bwd.h", "zz_mfma.h", "zz_device.h",
+                  "zz_util.hip", "zz_internal.h", "../build.py"]
 _NAMES = ["fwd_step_kernel", "bwd_dkv_kernel", "bwd_dq_kernel", "permute_kernel", "cast_rows_kernel",
           "bwd_pre_kernel", "lse_merge_kernel", "debug_mask_kernel"]
 
