@@ -69,17 +69,22 @@ int64_t tile_pairs(int kind, int32_t q0, int32_t q1, int32_t k0, int32_t k1, int
 }
 
 // Launch order of a pass's items, longest first.  When a query-major walk
-// (forward, dQ) mixes long and short items -- median work under a quarter of
-// the largest, as with packed short documents -- the order alternates
-// longest and shortest, so the latency-bound short items run next to long
-// ones instead of all together at the end of the launch (15 documents of
-// 64-16384 tokens: dQ 4-8% and forward 1-1.6% faster).  Items of one long
-// sequence are close in size and keep longest-first (alternating cost them
-// 0.2-0.4%), and the key-major dK/dV walk always does (alternating made it
-// 13-19% slower).
-void launch_order(const PassTables &t, const std::vector<int64_t> &item_work, std::vector<int32_t> &ord) {
+// (forward, dQ) of many workgroups mixes long and short items -- median work
+// under a quarter of the largest, as with packed short documents -- the
+// order alternates longest and shortest, so the latency-bound short items
+// run next to long ones instead of all together at the end of the launch
+// (15 documents of 64-16384 tokens: dQ 4-8% and forward 1-1.6% faster).
+// Items of one long sequence are close in size and keep longest-first
+// (alternating cost them 0.2-0.4%), as do launches of only a few rounds of
+// workgroups (alternating cost 8192 tokens of 5 documents 5%), and the
+// key-major dK/dV walk always does (alternating made it 13-19% slower).
+void launch_order(const zz_plan *p, const PassTables &t, const std::vector<int64_t> &item_work,
+                  std::vector<int32_t> &ord) {
     std::stable_sort(ord.begin(), ord.end(), [&](int32_t x, int32_t y) { return item_work[x] > item_work[y]; });
     if (t.key_major) return;
+    // a launch of a few rounds of workgroups (8192 = 16 rounds of two per CU
+    // on 256 CUs) finishes soonest with the longest items started first
+    if ((int64_t)ord.size() * p->hq < 8192) return;
     // items with no visible tile (kept by the forward only to clear their
     // rows) cost nothing and do not count
     size_t busy = 0;
@@ -170,7 +175,7 @@ void build_pass(zz_plan *p, PassTables &t) {
         const int64_t b = t.rank_off[(size_t)s * cp], e = (int64_t)t.items.size();
         std::vector<int32_t> ord;
         for (int64_t u = b; u < e; ++u) ord.push_back((int32_t)u);
-        launch_order(t, item_work, ord);
+        launch_order(p, t, item_work, ord);
         t.order.insert(t.order.end(), ord.begin(), ord.end());
     }
     t.rank_off[(size_t)cp * cp] = (int64_t)t.items.size();
@@ -255,7 +260,7 @@ void build_gathered_pass(zz_plan *p, PassTables &t) {
     t.rank_off[(size_t)cp] = (int64_t)t.items.size();
     std::vector<int32_t> ord;
     for (size_t u = 0; u < t.items.size(); ++u) ord.push_back((int32_t)u);
-    launch_order(t, item_work, ord);
+    launch_order(p, t, item_work, ord);
     t.order = ord;
     t.order_off[1] = (int64_t)t.order.size();
 }
