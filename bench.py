@@ -369,6 +369,11 @@ def main():
         "useful_fwd_tflop": round(fwd_flops / 1e12, 3),
         "tile_efficiency": round(useful_pairs / issued_pairs, 4),
         "kernels_ms": {n: round(v["mean_ms"], 4) for n, v in ks.items()},
+        # algorithmic TFLOP/s of every MFMA kernel (executed products, the
+        # recomputed ones in dQ included) and its fraction of the peak
+        "kernels_tflops": {n: {"tflops": round(per_launch[n] / (v["mean_ms"] * 1e-3) / 1e12, 2),
+                               "frac": round(per_launch[n] / (v["mean_ms"] * 1e-3) / 1e12 / peak, 4)}
+                           for n, v in ks.items() if n in per_launch},
         "roofline": {
             "kernel": dom,
             "bound": "mfma",
