@@ -34,7 +34,10 @@
  *    memory; zz_plan_destroy frees it.
  *  - Errors.  Every call returns zz_status; nothing throws across the ABI.
  *    Arguments are checked on the host before any launch; device pointers
- *    must be 16-byte aligned (ZZ_ERR_ALIGN).  A failed launch returns
+ *    must be 16-byte aligned (ZZ_ERR_ALIGN).  A buffer a call writes must
+ *    not overlap any other buffer of that call, measured over the whole
+ *    buffer the plan's shape gives it (ZZ_ERR_ARG, naming the two buffers);
+ *    buffers that are only read may share memory.  A failed launch returns
  *    ZZ_ERR_HIP; zz_last_error() gives a message for the calling thread.
  *  - Execution.  Device calls are asynchronous on the given stream (a
  *    hipStream_t passed as void*; NULL = the default stream).  A plan is
@@ -239,7 +242,7 @@ zz_status zz_lse_merge(float *o_acc, float *lse_acc, const float *o_part, const 
 /*
  * o_out = o_acc converted to the plan dtype (round to nearest even for bf16).
  * o_acc fp32 [T, hq, d] zigzag layout.  unpermute = 1 writes o_out in packed
- * token order, 0 keeps the zigzag order.  o_out must not alias o_acc.
+ * token order, 0 keeps the zigzag order.  o_out must not overlap o_acc.
  */
 zz_status zz_finalize_fwd(const zz_plan *plan, const float *o_acc, void *o_out, int32_t unpermute,
                           void *stream);
@@ -285,7 +288,8 @@ zz_status zz_varlen_ring_step_bwd_dq(const zz_plan *plan, int32_t rank, int32_t 
 
 /*
  * Gradients to the plan dtype: dq_out [T,hq,d], dk_out/dv_out [T,hkv,d];
- * unpermute = 1 writes packed token order.  Outputs must not alias inputs.
+ * unpermute = 1 writes packed token order.  No output may overlap another
+ * output or an input.
  */
 zz_status zz_finalize_bwd(const zz_plan *plan, const float *dq_acc, const float *dk_acc,
                           const float *dv_acc, void *dq_out, void *dk_out, void *dv_out,

@@ -40,6 +40,37 @@ zz_status check_ptrs(std::initializer_list<const void *> ps) {
     return ZZ_OK;
 }
 
+// One buffer of a call: its extent in bytes and whether the call writes it.
+struct Span {
+    const char *name;
+    const void *p;
+    uint64_t bytes;
+    bool written;
+};
+
+// A buffer the call writes must not overlap any other buffer of the call
+// (the kernels read and write whole rows in parallel, so an overlap is a
+// race); buffers that are only read may share memory.
+zz_status check_disjoint(std::initializer_list<Span> spans) {
+    for (const Span &a : spans) {
+        if (!a.written || a.bytes == 0) continue;
+        const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.bytes;
+        for (const Span &b : spans) {
+            if (&a == &b || b.bytes == 0) continue;
+            const uintptr_t b0 = (uintptr_t)b.p, b1 = b0 + b.bytes;
+            if (a0 < b1 && b0 < a1)
+                return fail(ZZ_ERR_ARG, std::string("buffers overlap: ") + a.name + " and " + b.name);
+        }
+    }
+    return ZZ_OK;
+}
+
+// Whole-buffer extents of the plan's tensors.
+uint64_t rows_bytes(const zz_plan *p, int32_t heads, bool fp32) {
+    return (uint64_t)p->T * heads * p->d * (fp32 || p->dtype == ZZ_F32 ? 4u : 2u);
+}
+uint64_t stat_bytes(const zz_plan *p) { return (uint64_t)p->T * p->hq * 4u; }
+
 zz_status hip_status(hipError_t e, const char *what) {
     if (e == hipSuccess) return ZZ_OK;
     return fail(ZZ_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
@@ -211,7 +242,8 @@ zz_status zz_zigzag_permute(const zz_plan *p, const void *x_packed, void *x_zz, 
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_ptrs({x_packed, x_zz}));
     if (row_bytes <= 0 || row_bytes % 16) return fail(ZZ_ERR_ALIGN, "row_bytes must be a positive multiple of 16");
-    if (x_packed == x_zz) return fail(ZZ_ERR_ARG, "in-place permute is not supported");
+    ZZ_TRY(check_disjoint({{"x_packed", x_packed, (uint64_t)p->T * row_bytes, false},
+                           {"x_zz", x_zz, (uint64_t)p->T * row_bytes, true}}));
     return hip_status(zz::launch_permute(p, x_packed, x_zz, row_bytes, false, (hipStream_t)stream), "permute");
 }
 
@@ -220,7 +252,8 @@ zz_status zz_zigzag_unpermute(const zz_plan *p, const void *x_zz, void *x_packed
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_ptrs({x_packed, x_zz}));
     if (row_bytes <= 0 || row_bytes % 16) return fail(ZZ_ERR_ALIGN, "row_bytes must be a positive multiple of 16");
-    if (x_packed == x_zz) return fail(ZZ_ERR_ARG, "in-place unpermute is not supported");
+    ZZ_TRY(check_disjoint({{"x_zz", x_zz, (uint64_t)p->T * row_bytes, false},
+                           {"x_packed", x_packed, (uint64_t)p->T * row_bytes, true}}));
     return hip_status(zz::launch_permute(p, x_zz, x_packed, row_bytes, true, (hipStream_t)stream), "unpermute");
 }
 
@@ -230,6 +263,11 @@ zz_status zz_varlen_ring_step_fwd(const zz_plan *p, int32_t rank, int32_t step, 
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_rank_step(p, rank, step, true));
     ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, o_acc, lse_acc}));
+    ZZ_TRY(check_disjoint({{"q_zz", q_zz, rows_bytes(p, p->hq, false), false},
+                           {"k_zz", k_zz, rows_bytes(p, p->hkv, false), false},
+                           {"v_zz", v_zz, rows_bytes(p, p->hkv, false), false},
+                           {"o_acc", o_acc, rows_bytes(p, p->hq, true), true},
+                           {"lse_acc", lse_acc, stat_bytes(p), true}}));
     if (merge != 0 && merge != 1) return fail(ZZ_ERR_ARG, "merge must be 0 or 1");
     return hip_status(zz::launch_fwd_step(p, rank, step, q_zz, k_zz, v_zz, o_acc, lse_acc, merge,
                                           (hipStream_t)stream), "varlen_ring_step_fwd");
@@ -240,6 +278,11 @@ zz_status zz_varlen_gathered_fwd(const zz_plan *p, int32_t rank, const void *q_z
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_rank_step(p, rank, 0, true));
     ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, o, lse}));
+    ZZ_TRY(check_disjoint({{"q_zz", q_zz, rows_bytes(p, p->hq, false), false},
+                           {"k_zz", k_zz, rows_bytes(p, p->hkv, false), false},
+                           {"v_zz", v_zz, rows_bytes(p, p->hkv, false), false},
+                           {"o", o, rows_bytes(p, p->hq, true), true},
+                           {"lse", lse, stat_bytes(p), true}}));
     return hip_status(zz::launch_fwd_gathered(p, rank, q_zz, k_zz, v_zz, o, lse, (hipStream_t)stream),
                       "varlen_gathered_fwd");
 }
@@ -250,6 +293,15 @@ zz_status zz_varlen_gathered_bwd(const zz_plan *p, int32_t rank, const void *q_z
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_rank_step(p, rank, 0, true));
     ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv}));
+    ZZ_TRY(check_disjoint({{"q_zz", q_zz, rows_bytes(p, p->hq, false), false},
+                           {"k_zz", k_zz, rows_bytes(p, p->hkv, false), false},
+                           {"v_zz", v_zz, rows_bytes(p, p->hkv, false), false},
+                           {"do_zz", do_zz, rows_bytes(p, p->hq, false), false},
+                           {"lse", lse, stat_bytes(p), false},
+                           {"delta", delta, stat_bytes(p), false},
+                           {"dq", dq, rows_bytes(p, p->hq, true), true},
+                           {"dk", dk, rows_bytes(p, p->hkv, true), true},
+                           {"dv", dv, rows_bytes(p, p->hkv, true), true}}));
     return hip_status(zz::launch_bwd_gathered(p, rank, q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv,
                                               (hipStream_t)stream), "varlen_gathered_bwd");
 }
@@ -259,6 +311,9 @@ zz_status zz_lse_merge(float *o_acc, float *lse_acc, const float *o_part, const 
     ZZ_TRY(check_ptrs({o_acc, lse_acc, o_part, lse_part}));
     if (rows < 0 || heads < 1 || head_dim < 1 || head_dim % 4) return fail(ZZ_ERR_ARG, "bad merge shape (head_dim % 4 == 0)");
     if (rows == 0) return ZZ_OK;
+    const uint64_t ob = (uint64_t)rows * heads * head_dim * 4u, lb = (uint64_t)rows * heads * 4u;
+    ZZ_TRY(check_disjoint({{"o_acc", o_acc, ob, true}, {"lse_acc", lse_acc, lb, true},
+                           {"o_part", o_part, ob, false}, {"lse_part", lse_part, lb, false}}));
     return hip_status(zz::launch_lse_merge(o_acc, lse_acc, o_part, lse_part, rows, heads, head_dim,
                                            (hipStream_t)stream), "lse_merge");
 }
@@ -267,7 +322,8 @@ zz_status zz_finalize_fwd(const zz_plan *p, const float *o_acc, void *o_out, int
                           void *stream) {
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_ptrs({o_acc, o_out}));
-    if ((const void *)o_acc == o_out) return fail(ZZ_ERR_ARG, "o_out must not alias o_acc");
+    ZZ_TRY(check_disjoint({{"o_acc", o_acc, rows_bytes(p, p->hq, true), false},
+                           {"o_out", o_out, rows_bytes(p, p->hq, false), true}}));
     return hip_status(zz::launch_cast_rows(p, o_acc, o_out, p->hq, unpermute != 0, (hipStream_t)stream),
                       "finalize_fwd");
 }
@@ -276,6 +332,9 @@ zz_status zz_bwd_preprocess(const zz_plan *p, const void *o_zz, const void *do_z
                             void *stream) {
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_ptrs({o_zz, do_zz, delta}));
+    ZZ_TRY(check_disjoint({{"o_zz", o_zz, rows_bytes(p, p->hq, false), false},
+                           {"do_zz", do_zz, rows_bytes(p, p->hq, false), false},
+                           {"delta", delta, stat_bytes(p), true}}));
     return hip_status(zz::launch_bwd_pre(p, o_zz, do_zz, delta, (hipStream_t)stream), "bwd_preprocess");
 }
 
@@ -286,6 +345,15 @@ zz_status zz_varlen_ring_step_bwd(const zz_plan *p, int32_t rank, int32_t step, 
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_rank_step(p, rank, step, true));
     ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc, dk_acc, dv_acc}));
+    ZZ_TRY(check_disjoint({{"q_zz", q_zz, rows_bytes(p, p->hq, false), false},
+                           {"k_zz", k_zz, rows_bytes(p, p->hkv, false), false},
+                           {"v_zz", v_zz, rows_bytes(p, p->hkv, false), false},
+                           {"do_zz", do_zz, rows_bytes(p, p->hq, false), false},
+                           {"lse", lse, stat_bytes(p), false},
+                           {"delta", delta, stat_bytes(p), false},
+                           {"dq_acc", dq_acc, rows_bytes(p, p->hq, true), true},
+                           {"dk_acc", dk_acc, rows_bytes(p, p->hkv, true), true},
+                           {"dv_acc", dv_acc, rows_bytes(p, p->hkv, true), true}}));
     if (accumulate != 0 && accumulate != 1) return fail(ZZ_ERR_ARG, "accumulate must be 0 or 1");
     return hip_status(zz::launch_bwd_step(p, rank, step, q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc,
                                           dk_acc, dv_acc, accumulate, 3, (hipStream_t)stream),
@@ -299,6 +367,14 @@ zz_status zz_varlen_ring_step_bwd_dkv(const zz_plan *p, int32_t rank, int32_t st
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_rank_step(p, rank, step, true));
     ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dk_acc, dv_acc}));
+    ZZ_TRY(check_disjoint({{"q_zz", q_zz, rows_bytes(p, p->hq, false), false},
+                           {"k_zz", k_zz, rows_bytes(p, p->hkv, false), false},
+                           {"v_zz", v_zz, rows_bytes(p, p->hkv, false), false},
+                           {"do_zz", do_zz, rows_bytes(p, p->hq, false), false},
+                           {"lse", lse, stat_bytes(p), false},
+                           {"delta", delta, stat_bytes(p), false},
+                           {"dk_acc", dk_acc, rows_bytes(p, p->hkv, true), true},
+                           {"dv_acc", dv_acc, rows_bytes(p, p->hkv, true), true}}));
     if (accumulate != 0 && accumulate != 1) return fail(ZZ_ERR_ARG, "accumulate must be 0 or 1");
     return hip_status(zz::launch_bwd_step(p, rank, step, q_zz, k_zz, v_zz, do_zz, lse, delta, nullptr,
                                           dk_acc, dv_acc, accumulate, 1, (hipStream_t)stream),
@@ -312,6 +388,13 @@ zz_status zz_varlen_ring_step_bwd_dq(const zz_plan *p, int32_t rank, int32_t ste
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_rank_step(p, rank, step, true));
     ZZ_TRY(check_ptrs({q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc}));
+    ZZ_TRY(check_disjoint({{"q_zz", q_zz, rows_bytes(p, p->hq, false), false},
+                           {"k_zz", k_zz, rows_bytes(p, p->hkv, false), false},
+                           {"v_zz", v_zz, rows_bytes(p, p->hkv, false), false},
+                           {"do_zz", do_zz, rows_bytes(p, p->hq, false), false},
+                           {"lse", lse, stat_bytes(p), false},
+                           {"delta", delta, stat_bytes(p), false},
+                           {"dq_acc", dq_acc, rows_bytes(p, p->hq, true), true}}));
     if (accumulate != 0 && accumulate != 1) return fail(ZZ_ERR_ARG, "accumulate must be 0 or 1");
     return hip_status(zz::launch_bwd_step(p, rank, step, q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc,
                                           nullptr, nullptr, accumulate, 2, (hipStream_t)stream),
@@ -323,6 +406,12 @@ zz_status zz_finalize_bwd(const zz_plan *p, const float *dq_acc, const float *dk
                           int32_t unpermute, void *stream) {
     ZZ_TRY(check_plan(p));
     ZZ_TRY(check_ptrs({dq_acc, dk_acc, dv_acc, dq_out, dk_out, dv_out}));
+    ZZ_TRY(check_disjoint({{"dq_acc", dq_acc, rows_bytes(p, p->hq, true), false},
+                           {"dk_acc", dk_acc, rows_bytes(p, p->hkv, true), false},
+                           {"dv_acc", dv_acc, rows_bytes(p, p->hkv, true), false},
+                           {"dq_out", dq_out, rows_bytes(p, p->hq, false), true},
+                           {"dk_out", dk_out, rows_bytes(p, p->hkv, false), true},
+                           {"dv_out", dv_out, rows_bytes(p, p->hkv, false), true}}));
     hipStream_t st = (hipStream_t)stream;
     ZZ_TRY(hip_status(zz::launch_cast_rows(p, dq_acc, dq_out, p->hq, unpermute != 0, st), "finalize_bwd dq"));
     ZZ_TRY(hip_status(zz::launch_cast_rows(p, dk_acc, dk_out, p->hkv, unpermute != 0, st), "finalize_bwd dk"));
