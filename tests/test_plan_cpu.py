@@ -74,6 +74,15 @@ def test_bad_rank_step_and_merge_flag_are_rejected_before_launch():
     assert L.zz_lse_merge(None, None, None, None, 4, 1, 8, None) == 1
     assert L.zz_lse_merge(ctypes.c_void_p(8), ctypes.c_void_p(16), ctypes.c_void_p(16),
                           ctypes.c_void_p(16), 4, 1, 8, None) == 4
+    # a written buffer overlapping another one of the call is rejected before
+    # any launch (o: 4 rows x 1 head x 8 = 128 bytes; lse: 16 bytes)
+    base = 1 << 20
+    rc = L.zz_lse_merge(ctypes.c_void_p(base), ctypes.c_void_p(base + 4096), ctypes.c_void_p(base + 64),
+                        ctypes.c_void_p(base + 8192), 4, 1, 8, None)
+    assert rc == 1 and L.zz_last_error().decode() == "buffers overlap: o_acc and o_part"
+    rc = L.zz_lse_merge(ctypes.c_void_p(base), ctypes.c_void_p(base + 112), ctypes.c_void_p(base + 4096),
+                        ctypes.c_void_p(base + 8192), 4, 1, 8, None)
+    assert rc == 1 and L.zz_last_error().decode() == "buffers overlap: o_acc and lse_acc"
 
 
 WORK = {
