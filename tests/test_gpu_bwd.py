@@ -56,6 +56,20 @@ def test_backward_bf16(lengths, cp, hq, hkv, d, q_scale):
     check_grads(case, TOL["bf16"])
 
 
+def test_backward_with_dq_on_a_second_stream_is_bitwise_equal():
+    import torch
+    case = Case((64, 320, 128, 96), 4, 4, 2, 128, "bf16", 7, with_do=True)
+    o_acc, lse = zz.ring_attention_fwd(case.plan, case.qz, case.kz, case.vz)
+    o_zz = zz.finalize_fwd(case.plan, o_acc)
+    one = zz.ring_attention_bwd(case.plan, case.qz, case.kz, case.vz, o_zz, case.doz, lse)
+    side = torch.cuda.Stream()
+    for _ in range(2):   # the second call reuses the side stream after the first finished
+        two = zz.ring_attention_bwd(case.plan, case.qz, case.kz, case.vz, o_zz, case.doz, lse, dq_stream=side)
+        torch.cuda.synchronize()
+        for a, b in zip(one, two):
+            assert torch.equal(a, b)
+
+
 def test_backward_per_rank_equals_all_ranks():
     import torch
     case = Case((128, 256, 64), 2, 4, 2, 128, "bf16", 3, with_do=True)

@@ -409,17 +409,36 @@ def ring_attention_fwd(plan: Plan, q_zz, k_zz, v_zz, rank: int = ALL_RANKS, o_ac
     return o_acc, lse
 
 
-def ring_attention_bwd(plan: Plan, q_zz, k_zz, v_zz, o_zz, do_zz, lse, stream=None):
+def ring_attention_bwd(plan: Plan, q_zz, k_zz, v_zz, o_zz, do_zz, lse, stream=None, dq_stream=None):
     """All ring steps of the backward.  Step 0 (the diagonal shard, which
     touches every row) overwrites, later steps accumulate.  Returns fp32
-    (dq, dk, dv) in zigzag layout."""
+    (dq, dk, dv) in zigzag layout.
+
+    dq_stream: optional second stream for the dQ launches (the dK/dV and dQ
+    launches of a step write disjoint buffers); it waits for `stream` after
+    the pre-pass and `stream` waits for it at the end, so the results are the
+    same bits.  It pays off when a step's launches are only a few rounds of
+    workgroups (packings of short documents); with one long sequence the
+    concurrent grids run slower than one stream."""
     import torch
     dev = q_zz.device
-    delta = bwd_preprocess(plan, o_zz, do_zz, stream=stream)
+    base = stream if stream is not None else torch.cuda.current_stream()
+    delta = bwd_preprocess(plan, o_zz, do_zz, stream=base)
     dq = torch.empty((plan.total, plan.hq, plan.d), dtype=torch.float32, device=dev)
     dk = torch.empty((plan.total, plan.hkv, plan.d), dtype=torch.float32, device=dev)
     dv = torch.empty((plan.total, plan.hkv, plan.d), dtype=torch.float32, device=dev)
+    if dq_stream is None:
+        for s in range(plan.cp):
+            varlen_ring_step_bwd(plan, ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv,
+                                 accumulate=s > 0, stream=base)
+        return dq, dk, dv
+    dq_stream.wait_stream(base)
+    dq.record_stream(dq_stream)      # allocated here, used on the side stream
+    delta.record_stream(dq_stream)
     for s in range(plan.cp):
-        varlen_ring_step_bwd(plan, ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dq, dk, dv,
-                             accumulate=s > 0, stream=stream)
+        varlen_ring_step_bwd_dkv(plan, ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dk, dv,
+                                 accumulate=s > 0, stream=base)
+        varlen_ring_step_bwd_dq(plan, ALL_RANKS, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dq,
+                                accumulate=s > 0, stream=dq_stream)
+    base.wait_stream(dq_stream)
     return dq, dk, dv
