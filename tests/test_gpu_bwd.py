@@ -50,6 +50,8 @@ def test_backward_fp32(lengths, cp, hq, hkv, d):
     ((512,), 4, 8, 1, 128, 4.0),
     ((96, 160, 8), 2, 4, 2, 64, 1.0),    # head_dim 64
     ((40, 24, 200), 2, 2, 2, 32, 2.0),   # head_dim 32, MHA
+    ((36, 12, 60, 96), 3, 8, 2, 128, 1.0),  # CP not a power of two, GQA 4:1
+    ((72, 24), 1, 4, 1, 64, 2.0),        # one rank (only the diagonal step), GQA 4:1
 ])
 def test_backward_bf16(lengths, cp, hq, hkv, d, q_scale):
     case = Case(lengths, cp, hq, hkv, d, "bf16", 23, with_do=True, q_scale=q_scale)

@@ -141,6 +141,8 @@ def test_forward_c1_fp32_full():
     ((200, 56), 2, 4, 4, 64, "bf16", 1.0),            # bf16 head_dim 64, MHA
     ((36, 12, 60, 96), 3, 4, 2, 64, "f32", 1.0),      # CP not a power of two
     ((96, 36, 150), 3, 4, 2, 128, "bf16", 1.0),
+    ((96, 36, 150), 3, 8, 2, 128, "bf16", 2.0),       # GQA 4:1
+    ((72, 24), 1, 4, 1, 64, "bf16", 1.0),             # one rank, GQA 4:1
     ((64, 128, 320), 32, 2, 1, 32, "f32", 1.0),       # CP 32: one- and two-row chunks, 1024 rank-steps
 ])
 def test_forward_small_full(lengths, cp, hq, hkv, d, dtype, q_scale):
