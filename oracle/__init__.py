@@ -57,6 +57,8 @@ def lib():
             L.oracle_lse_merge.argtypes = [P, P, P, P, i64, i32, i32]
             L.oracle_attn_bwd.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, P, P, P]
             L.oracle_attn_bwd_dq_rows.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, P, P, i64, P]
+            L.oracle_attn_bwd_dkv_rows.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f64, P, P, i64, P,
+                                                   P, P, P, P]
             L.oracle_tiles.argtypes = [P, i32, i32, i32, i32, i32, i32, P, i64, P]
             L.oracle_rank_pairs.argtypes = [P, i32, i32, P]
             L.oracle_num_threads.argtypes = []
@@ -211,6 +213,41 @@ def attn_bwd_dq_rows(q, k, v, dout, cu, scale: float, rows, heads):
     lib().oracle_attn_bwd_dq_rows(_p(q), _p(k), _p(v), _p(do), _p(cu), len(cu) - 1, hq, hkv, d,
                                   scale, _p(rows), _p(heads), n, _p(dq))
     return dq
+
+
+def attn_bwd_dkv_rows(q, k, v, dout, cu, scale: float, rows, kv_heads, heads_on=None, row_stats=None):
+    """dK, dV for the given (packed key row, key/value head) pairs: dk [n,d], dv [n,d].
+
+    ``heads_on``: query heads to sum over (default: all).  Pass a subset only
+    when dO is identically zero on every other head of the selected groups;
+    those heads contribute exactly zero and their row statistics are then not
+    computed.  ``row_stats``: optional (lse, dsum), float64 [hq, T] in packed
+    rows, each needed row's LSE and D = <dO_q, O_q> from this oracle's own
+    forward (``attn_fwd_rows``); without it they are computed here."""
+    q, k, v, do, cu = _f32(q), _f32(k), _f32(v), _f32(dout), _cu(cu)
+    T, hq, d = q.shape
+    hkv = k.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    kv_heads = np.ascontiguousarray(kv_heads, dtype=np.int32)
+    n = len(rows)
+    on = None
+    if heads_on is not None:
+        on = np.zeros(hq, dtype=np.int32)
+        on[np.asarray(list(heads_on), dtype=np.int64)] = 1
+    lse = dsum = None
+    if row_stats is not None:
+        lse = np.ascontiguousarray(row_stats[0], dtype=np.float64)
+        dsum = np.ascontiguousarray(row_stats[1], dtype=np.float64)
+        if lse.shape != (hq, T) or dsum.shape != (hq, T):
+            raise ValueError("row_stats must be two float64 [hq, T] tables")
+    dk = np.empty((n, d), dtype=np.float64)
+    dv = np.empty((n, d), dtype=np.float64)
+    lib().oracle_attn_bwd_dkv_rows(_p(q), _p(k), _p(v), _p(do), _p(cu), len(cu) - 1, hq, hkv, d,
+                                   scale, _p(rows), _p(kv_heads), n,
+                                   _p(on) if on is not None else None,
+                                   _p(lse) if lse is not None else None,
+                                   _p(dsum) if dsum is not None else None, _p(dk), _p(dv))
+    return dk, dv
 
 
 def tiles(cu, cp: int, rank: int, step: int, bm: int, bn: int) -> np.ndarray:

@@ -441,6 +441,87 @@ void oracle_attn_bwd_dq_rows(const float *q, const float *k, const float *v, con
     }
 }
 
+/*
+ * dK and dV for selected (packed key row, key/value head) pairs only:
+ * dk, dv [n,d].  Key row kp of head g collects, from every query head h of
+ * the group and every query row pq >= kp of its sequence,
+ *   dV += P_qk dO_q  and  dK += scale * dS_qk Q_q,
+ * with P = exp(S - LSE_q) and dS = P (dP - D_q) taken from the query row's own
+ * LSE and D (bwd_row_stats, the same definitions as oracle_attn_bwd), so the
+ * result is exact at any size.  head_on (int32[hq], or NULL for every head)
+ * leaves out heads with head_on[h] == 0: the caller uses it only for heads
+ * whose dO is identically zero, which add exactly nothing (dP = 0 and D = 0
+ * give dS = 0, and P dO = 0).  The row statistics of every (head, row) the
+ * selected keys need are computed once, before the sums -- unless the caller
+ * passes them: lse_in and dsum_in ([hq,T], both or neither) then hold each
+ * needed row's LSE and D = sum_k P_qk dP_qk = <dO_q, O_q> (O the row's
+ * attention output), e.g. from oracle_attn_fwd_rows of the same inputs.
+ */
+void oracle_attn_bwd_dkv_rows(const float *q, const float *k, const float *v, const float *dout,
+                              const int32_t *cu, int32_t nseq, int32_t hq, int32_t hkv, int32_t d,
+                              double scale, const int64_t *rows, const int32_t *kv_heads, int64_t n,
+                              const int32_t *head_on, const double *lse_in, const double *dsum_in,
+                              double *dk, double *dv) {
+    int64_t T = total_tokens(cu, nseq);
+    int32_t G = hq / hkv;
+    int64_t Lmax = max_len(cu, nseq);
+    /* need[h*T + pq]: the statistics of query row pq of head h are used */
+    uint8_t *need = (uint8_t *)calloc((size_t)hq * T, 1);
+    double *lse_own = NULL, *dsum_own = NULL;
+    if (!lse_in) {
+        lse_own = (double *)malloc(sizeof(double) * hq * T);
+        dsum_own = (double *)malloc(sizeof(double) * hq * T);
+    }
+    const double *lse = lse_in ? lse_in : lse_own;
+    const double *dsum = lse_in ? dsum_in : dsum_own;
+    for (int64_t t = 0; t < n; ++t) {
+        int32_t i = seq_of(cu, nseq, rows[t]);
+        for (int32_t h = kv_heads[t] * G; h < (kv_heads[t] + 1) * G; ++h) {
+            if (head_on && !head_on[h]) continue;
+            for (int64_t pq = rows[t]; pq < cu[i + 1]; ++pq) need[(size_t)h * T + pq] = 1;
+        }
+    }
+    if (!lse_in) {
+#pragma omp parallel
+        {
+            double *sbuf = (double *)malloc(sizeof(double) * Lmax);
+#pragma omp for schedule(dynamic, 16) collapse(2)
+            for (int32_t h = 0; h < hq; ++h)
+                for (int64_t p = 0; p < T; ++p)
+                    if (need[(size_t)h * T + p])
+                        bwd_row_stats(q, k, v, dout, cu, nseq, hq, hkv, d, scale, p, h, sbuf,
+                                      lse_own + (size_t)h * T + p, dsum_own + (size_t)h * T + p);
+            free(sbuf);
+        }
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t kp = rows[t];
+        int32_t g = kv_heads[t], i = seq_of(cu, nseq, kp);
+        const float *kr = k + ((size_t)kp * hkv + g) * d;
+        const float *vr = v + ((size_t)kp * hkv + g) * d;
+        double *dkr = dk + (size_t)t * d;
+        double *dvr = dv + (size_t)t * d;
+        for (int32_t e = 0; e < d; ++e) dkr[e] = dvr[e] = 0.0;
+        for (int32_t h = g * G; h < (g + 1) * G; ++h) {
+            if (head_on && !head_on[h]) continue;
+            for (int64_t pq = kp; pq < cu[i + 1]; ++pq) {
+                const float *qr = q + ((size_t)pq * hq + h) * d;
+                const float *dor = dout + ((size_t)pq * hq + h) * d;
+                double P = exp(scale * dot(qr, kr, d) - lse[(size_t)h * T + pq]);
+                double dS = P * (dot(dor, vr, d) - dsum[(size_t)h * T + pq]);
+                for (int32_t e = 0; e < d; ++e) {
+                    dvr[e] += P * (double)dor[e];
+                    dkr[e] += scale * dS * (double)qr[e];
+                }
+            }
+        }
+    }
+    free(need);
+    free(lse_own);
+    free(dsum_own);
+}
+
 /* ------------------------------------------------------------------------- */
 /* Tiles and work balance                                                    */
 /* ------------------------------------------------------------------------- */

@@ -21,11 +21,14 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "zigzag_extract_local
 # ---------------------------------------------------------------- helpers
 
 def split_like_extract_local(x: torch.Tensor, rank: int, world: int) -> torch.Tensor:
-    """The shard a rank keeps: cut into 2*world equal pieces, keep piece
-    `rank` and the piece mirrored from the end (ring-attention-pytorch issue
-    #20, extract_local snippet).  Written with torch.chunk / torch.cat."""
-    parts = x.chunk(2 * world, dim=0)
-    return torch.cat([parts[rank], parts[len(parts) - 1 - rank]], dim=0)
+    """The rows a rank keeps under the zigzag split that ring-attention-pytorch
+    issue #20 ("Zigzag attention support?") describes: with 2*world equal
+    chunks of c rows, rank r holds chunk r and then chunk 2*world-1-r, i.e. the
+    row indices [r*c, (r+1)*c) followed by [(2*world-1-r)*c, (2*world-r)*c)."""
+    c = x.shape[0] // (2 * world)
+    mirror = 2 * world - 1 - rank
+    idx = torch.cat([torch.arange(rank * c, (rank + 1) * c), torch.arange(mirror * c, (mirror + 1) * c)])
+    return x.index_select(0, idx)
 
 
 def packed_split(lengths, world):
@@ -467,3 +470,100 @@ def test_bwd_dq_rows_equal_full():
     heads = np.array([1, 0, 3, 2, 1])
     got = oracle.attn_bwd_dq_rows(q, k, v, do, cu, 0.35, rows, heads)
     assert np.abs(got - dq[rows, heads]).max() < 1e-14
+
+
+@pytest.mark.parametrize("lengths,hq,hkv,d", [((16, 8, 24), 4, 2, 8), ((32,), 8, 1, 16), ((12, 4), 2, 2, 4)])
+def test_bwd_dkv_rows_match_torch_autograd(lengths, hq, hkv, d):
+    """Every (key row, key/value head) of small packings against torch's
+    autograd through SDPA in float64."""
+    q, k, v, do = rand_inputs(29, lengths, hq, hkv, d, with_do=True)
+    scale = 1.0 / math.sqrt(d)
+    T = sum(lengths)
+    rows = np.repeat(np.arange(T), hkv)
+    kvh = np.tile(np.arange(hkv), T)
+    dk, dv = oracle.attn_bwd_dkv_rows(q, k, v, do, synthetic.make_cu_seqlens(lengths), scale, rows, kvh)
+    _, rk, rv = torch_reference_bwd(q, k, v, do, lengths, scale)
+    assert np.abs(dk - rk[rows, kvh]).max() < 1e-11
+    assert np.abs(dv - rv[rows, kvh]).max() < 1e-11
+
+
+def test_bwd_dkv_rows_zero_key_closed_form():
+    """K = 0: every visible key has weight 1/n_q (n_q = q - start + 1), O_q is
+    the running mean of V and D_q = <dO_q, O_q>, so per sequence and group
+      dV_k = sum_{q>=k} sum_h dO_q / n_q,
+      dK_k = scale * [ (sum_{q>=k} sum_h Q_q dO_q^T / n_q) V_k - sum_{q>=k} sum_h D_q Q_q / n_q ],
+    written here with reverse cumulative sums."""
+    lengths = [10, 6, 14]
+    hq, hkv, d = 4, 2, 5
+    G = hq // hkv
+    q, _, v, do = (x.double().numpy() for x in rand_inputs(31, lengths, hq, hkv, d, with_do=True))
+    k = np.zeros((sum(lengths), hkv, d))
+    scale = 0.45
+    cu = synthetic.make_cu_seqlens(lengths)
+    T = sum(lengths)
+    rows = np.repeat(np.arange(T), hkv)
+    kvh = np.tile(np.arange(hkv), T)
+    dk, dv = oracle.attn_bwd_dkv_rows(q.astype(np.float32), k.astype(np.float32), v.astype(np.float32),
+                                      do.astype(np.float32), cu, scale, rows, kvh)
+    q, v, do = q.astype(np.float32).astype(np.float64), v.astype(np.float32).astype(np.float64), \
+        do.astype(np.float32).astype(np.float64)
+    start = 0
+    for L in lengths:
+        n = np.arange(1, L + 1, dtype=np.float64)
+        for g in range(hkv):
+            hs = slice(g * G, (g + 1) * G)
+            vs = v[start:start + L, g]                                         # [L,d]
+            o = np.cumsum(vs, axis=0) / n[:, None]                             # running mean
+            dos = do[start:start + L, hs]                                      # [L,G,d]
+            qs = q[start:start + L, hs]
+            D = (dos * o[:, None, :]).sum(-1)                                  # [L,G]
+            rev = lambda x: np.cumsum(x[::-1], axis=0)[::-1]
+            want_dv = rev(dos.sum(1) / n[:, None])
+            A = rev(np.einsum("lgi,lgj->lij", qs, dos) / n[:, None, None])     # [L,d,d]
+            B = rev((D[:, :, None] * qs).sum(1) / n[:, None])                  # [L,d]
+            want_dk = scale * (np.einsum("lij,lj->li", A, vs) - B)
+            sel = (rows >= start) & (rows < start + L) & (kvh == g)
+            assert np.abs(dv[sel] - want_dv).max() < 1e-12
+            assert np.abs(dk[sel] - want_dk).max() < 1e-12
+        start += L
+
+
+def test_bwd_dkv_rows_heads_with_zero_upstream_add_nothing():
+    """The head subset a caller may pass is exact when dO vanishes on the
+    other heads: full-group sums equal the subset's, and both equal the full
+    backward's rows (sampled keys, first and last of each sequence included)."""
+    lengths = [24, 40]
+    hq, hkv, d = 8, 2, 8
+    q, k, v, do = rand_inputs(37, lengths, hq, hkv, d, with_do=True)
+    do = do.clone()
+    keep = [1, 6]
+    for h in range(hq):
+        if h not in keep:
+            do[:, h] = 0
+    cu = synthetic.make_cu_seqlens(lengths)
+    rows = np.array([0, 23, 24, 63, 5, 40, 12])
+    kvh = np.array([0, 1, 1, 0, 1, 0, 0])
+    full = oracle.attn_bwd_dkv_rows(q, k, v, do, cu, 0.3, rows, kvh)
+    sub = oracle.attn_bwd_dkv_rows(q, k, v, do, cu, 0.3, rows, kvh, heads_on=keep)
+    _, rk, rv = torch_reference_bwd(q, k, v, do, lengths, 0.3)
+    for a, b, ref in ((full[0], sub[0], rk), (full[1], sub[1], rv)):
+        assert np.array_equal(a, b)
+        assert np.abs(a - ref[rows, kvh]).max() < 1e-11
+
+
+def test_bwd_dkv_rows_with_forward_row_stats():
+    """Row statistics taken from the oracle's forward (LSE, and D = <dO, O>)
+    give the same dK, dV as the ones the function computes itself
+    (D = sum_k P dP): the two definitions of D agree."""
+    lengths = [20, 44]
+    hq, hkv, d = 4, 2, 8
+    q, k, v, do = rand_inputs(41, lengths, hq, hkv, d, with_do=True)
+    cu = synthetic.make_cu_seqlens(lengths)
+    o, lse = oracle.attn_fwd(q, k, v, cu, 0.3)
+    dsum = (o * do.double().numpy()).sum(-1).T.copy()          # [hq, T]
+    rows = np.array([0, 19, 20, 63, 7, 33, 50])
+    kvh = np.array([1, 0, 1, 1, 0, 0, 1])
+    own = oracle.attn_bwd_dkv_rows(q, k, v, do, cu, 0.3, rows, kvh)
+    given = oracle.attn_bwd_dkv_rows(q, k, v, do, cu, 0.3, rows, kvh, row_stats=(lse, dsum))
+    for a, b in zip(own, given):
+        assert np.abs(a - b).max() < 1e-12
