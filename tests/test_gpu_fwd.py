@@ -121,7 +121,7 @@ def check_full(case, o_acc, lse, out, tol):
     assert max_abs(n_l, lw) < tol["lse"]
     fo = to_np(out)
     assert max_abs(fo, ow) < tol["abs"]
-    assert rel_l2(fo, ow) < max(tol["rel"], 4e-3)
+    assert rel_l2(fo, ow) < tol["rel"]
 
 
 def test_forward_c1_fp32_full():

@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import synthetic
-from zz_testlib import TOL, Case, max_abs, rel_l2, to_np
+from zz_testlib import TOL, Case, check_grad, max_abs, rel_l2, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -105,11 +105,9 @@ def test_gathered_backward_matches_oracle(lengths, cp, hq, hkv, d, dtype):
     case = Case(lengths, cp, hq, hkv, d, dtype, 37, with_do=True)
     got = gathered_grads(case)
     want = oracle.attn_bwd(case.q, case.k, case.v, case.do, case.cu, case.scale)
-    tol = TOL[dtype]
+    tag = "gathered %s cp=%d hq=%d hkv=%d d=%d %s" % (lengths, cp, hq, hkv, d, dtype)
     for name, g, w in zip(("dq", "dk", "dv"), got, want):
-        gate = tol["abs"] * max(1.0, float(np.abs(w).max()))
-        assert max_abs(g, w) < gate, (name, max_abs(g, w), gate)
-        assert rel_l2(g, w) < tol["rel"], (name, rel_l2(g, w))
+        check_grad(name, g, w, TOL[dtype], 1.0, tag)
 
 
 def test_gathered_backward_per_rank_equals_all_ranks():
