@@ -84,7 +84,14 @@ const char *zz_last_error(void);
 /* ------------------------------------------------------------------ plan */
 
 /*
- * Build a plan for one packed batch.
+ * Build a plan for one packed batch.  The zigzag split of each sequence into
+ * 2*cp equal chunks, rank r holding chunk r then chunk 2*cp-1-r, is the one of
+ * ring-attention-pytorch issue #20 ("Zigzag attention support?", the
+ * extract_local snippet); the lengths arrive as a list as in EasyDeL issue
+ * #129 ("Attention Mask for Packed Sequences (via Attention Bias)", the
+ * packed-batch request); the divisibility check mirrors the assertion that
+ * FlagScale PR #910 ("[Train] Support custom attention with context
+ * parallel", flex-attention notes) places on sequence lengths under CP.
  *  cu_seqlens  host int32[nseq+1], cu[0] = 0, strictly increasing; every
  *              length L_i = cu[i+1]-cu[i] must be a multiple of 2*cp (the
  *              zigzag split needs 2*cp equal chunks per sequence).
@@ -128,7 +135,9 @@ zz_status zz_plan_tile_shape(const zz_plan *plan, zz_pass pass, int32_t *bm, int
 
 /*
  * Tiles that hold at least one visible (query, key) pair in ring step
- * (rank, step), in canonical order sorted by (q0, k0): out[5*t .. 5*t+4] =
+ * (rank, step) -- the pruning of fully masked work that FlagScale PR #910
+ * ("[Train] Support custom attention with context parallel", description)
+ * lists -- in canonical order sorted by (q0, k0): out[5*t .. 5*t+4] =
  * q0, q1, k0, k1, kind with rank-local query rows [q0,q1) and shard-local key
  * rows [k0,k1); kind is ZZ_TILE_FULL or ZZ_TILE_PARTIAL.  Tiles with no
  * visible pair are never listed and never visited by the kernels.
@@ -157,10 +166,22 @@ zz_status zz_plan_gathered_tiles(const zz_plan *plan, zz_pass pass, int32_t owne
 /*
  * Pair counts for rank/step (either may be ZZ_ALL_RANKS / ZZ_ALL_STEPS):
  * useful = visible (query, key) pairs per head; issued = pairs covered by the
- * pass's visited tiles (what the MFMA units process).
+ * pass's visited tiles (what the MFMA units process).  The per-rank balance
+ * these counts measure is the point of the zigzag split: causal work piles up
+ * on the late ranks of a contiguous split (MiniMax-01 issue #6, "Question
+ * about varlen ring attention"; ring-attention-pytorch issue #20).
+ * Errors: ZZ_ERR_ARG (null plan, bad pass, rank or step out of range).
  */
 zz_status zz_plan_pair_counts(const zz_plan *plan, zz_pass pass, int32_t rank, int32_t step,
                               int64_t *useful, int64_t *issued);
+
+/*
+ * Useful (visible) pairs per head of every rank over the whole ring:
+ * out int64[cp] (host), out[r] = sum over steps of rank r's visible pairs,
+ * equal to sum_i L_i (L_i + 1) / (2 cp) on every rank under the zigzag split
+ * (same passages as zz_plan_pair_counts).  Errors: ZZ_ERR_ARG.
+ */
+zz_status zz_plan_rank_useful_pairs(const zz_plan *plan, int64_t *out);
 
 /* ------------------------------------------------------------ device ops */
 
@@ -235,6 +256,13 @@ zz_status zz_varlen_gathered_bwd(const zz_plan *plan, int32_t rank, const void *
  * Standalone log-sum-exp merge: (o_acc, lse_acc) <- merge with (o_part,
  * lse_part).  o: fp32 [rows, heads, head_dim]; lse: fp32 [heads, rows].
  * (0, -inf) is the identity; two -inf rows give (0, -inf).
+ * The pages state that ring steps emit partial outputs that are combined
+ * (FlagScale PR #910, per-step forward of the ring driver) but give no
+ * formula: this natural-log log-sum-exp merge, L = log(e^a + e^b),
+ * O = e^(a-L) O_a + e^(b-L) O_b in fp32, is this library's reading of that
+ * silence (the plainest combination of two softmaxes over disjoint key sets).
+ * o_acc / lse_acc must not overlap o_part / lse_part (ZZ_ERR_ARG).
+ * Errors: ZZ_ERR_ARG, ZZ_ERR_ALIGN, ZZ_ERR_HIP.
  */
 zz_status zz_lse_merge(float *o_acc, float *lse_acc, const float *o_part, const float *lse_part,
                        int64_t rows, int32_t heads, int32_t head_dim, void *stream);
@@ -242,7 +270,10 @@ zz_status zz_lse_merge(float *o_acc, float *lse_acc, const float *o_part, const 
 /*
  * o_out = o_acc converted to the plan dtype (round to nearest even for bf16).
  * o_acc fp32 [T, hq, d] zigzag layout.  unpermute = 1 writes o_out in packed
- * token order, 0 keeps the zigzag order.  o_out must not overlap o_acc.
+ * token order, 0 keeps the zigzag order (MaxText PR #1133, "Add Context
+ * Parallelism support to cudnn Flash Attention", review: the reordered
+ * tokens are the framework's to restore).  o_out must not overlap o_acc.
+ * Errors: ZZ_ERR_ARG, ZZ_ERR_ALIGN, ZZ_ERR_STATE, ZZ_ERR_HIP.
  */
 zz_status zz_finalize_fwd(const zz_plan *plan, const float *o_acc, void *o_out, int32_t unpermute,
                           void *stream);
@@ -250,7 +281,12 @@ zz_status zz_finalize_fwd(const zz_plan *plan, const float *o_acc, void *o_out, 
 /*
  * Backward pre-pass: delta[h, z] = sum_e dO[z,h,e] * O[z,h,e] in fp32, from
  * the forward output O and upstream gradient dO (plan dtype, zigzag layout
- * [T, hq, d]).  delta fp32 [hq, T].
+ * [T, hq, d]).  delta fp32 [hq, T].  FlagScale PR #910 ("[Train] Support
+ * custom attention with context parallel", description) names a per-step
+ * backward of the ring driver without its arithmetic; delta is the row term
+ * of the softmax gradient, dS = P (dP - delta), computed once per backward
+ * from the final O so that every step can use it.
+ * Errors: ZZ_ERR_ARG, ZZ_ERR_ALIGN, ZZ_ERR_STATE, ZZ_ERR_HIP.
  */
 zz_status zz_bwd_preprocess(const zz_plan *plan, const void *o_zz, const void *do_zz, float *delta,
                             void *stream);
@@ -296,8 +332,10 @@ zz_status zz_finalize_bwd(const zz_plan *plan, const float *dq_acc, const float 
                           int32_t unpermute, void *stream);
 
 /*
- * Debug: the visibility a pass's kernels apply in ring step (rank, step),
- * walking the same device tile lists and the same in-tile mask:
+ * Debug: the visibility a pass's kernels apply in ring step (rank, step) --
+ * the causal mask (MaxText PR #1133, description: CP attention is causal) and
+ * the document mask (EasyDeL issue #129: no attention across packed
+ * examples) -- walking the same device tile lists and the same in-tile mask:
  * d_mask uint8 [(T/cp) x (T/cp)], row = rank-local query row, column =
  * shard-local key row; 1 = visible.  Every byte is written.
  */

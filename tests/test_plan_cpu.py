@@ -161,6 +161,7 @@ def test_rank_pairs_oracle_agrees_with_plan():
     want = oracle.rank_pairs(cu, cp)
     got = np.array([p.pair_counts(r)[0] for r in range(cp)])
     assert np.array_equal(got, want)
+    assert np.array_equal(p.rank_useful_pairs(), want)
 
 
 def test_contiguous_split_would_be_unbalanced():

@@ -31,8 +31,8 @@ ALL_STEPS = -1
 F32, BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# ZZ_LIBRARY may point at another build of libzz (e.g. a tuning variant).
-_LIB_PATH = os.environ.get("ZZ_LIBRARY") or os.path.join(_HERE, "libzz.so")
+# The library built in-tree next to this file; there is no other search path.
+_LIB_PATH = os.path.join(_HERE, "libzz.so")
 _lib = None
 
 
@@ -68,6 +68,7 @@ def lib():
         "zz_plan_tiles": ([P, i32, i32, i32, P, i64, P], i32),
         "zz_plan_gathered_tiles": ([P, i32, i32, P, i64, P], i32),
         "zz_plan_pair_counts": ([P, i32, i32, i32, P, P], i32),
+        "zz_plan_rank_useful_pairs": ([P, P], i32),
         "zz_zigzag_permute": ([P, P, P, i64, P], i32),
         "zz_zigzag_unpermute": ([P, P, P, i64, P], i32),
         "zz_varlen_ring_step_fwd": ([P, i32, i32, P, P, P, P, P, i32, P], i32),
@@ -212,6 +213,13 @@ class Plan:
         _check(lib().zz_plan_pair_counts(self._h, pass_, rank, step, ctypes.byref(u), ctypes.byref(i)),
                "zz_plan_pair_counts")
         return u.value, i.value
+
+    def rank_useful_pairs(self) -> np.ndarray:
+        """Visible (query, key) pairs per head of each rank over the whole ring: int64 [cp]."""
+        out = np.empty(self.cp, dtype=np.int64)
+        _check(lib().zz_plan_rank_useful_pairs(self._h, out.ctypes.data_as(ctypes.c_void_p)),
+               "zz_plan_rank_useful_pairs")
+        return out
 
 
 # ----------------------------------------------------------------- device ops

@@ -40,10 +40,9 @@ def common_flags():
             "-I" + os.path.join(HERE, "..", "include")]
 
 
-def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
-    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + common_flags() + SCHED_FLAGS.get(src, []) + ["-D" + d for d in defines] + \
-        ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + common_flags() + SCHED_FLAGS.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -52,12 +51,12 @@ def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, build_dir: str = BUILD, defines=()) -> str:
-    """Compile every source and link ``out`` (``defines``: extra -D macros for
-    tuning variants, built to their own ``build_dir``)."""
-    os.makedirs(build_dir, exist_ok=True)
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``libzz.so`` next to this file."""
+    os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+        objs = list(ex.map(_compile, SOURCES))
+    out = LIB
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

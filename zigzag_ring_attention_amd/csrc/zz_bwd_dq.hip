@@ -11,11 +11,6 @@
 
 #include "zz_bwd.h"
 
-// Waves per SIMD the kernel is compiled for (register budget 512 / waves).
-#ifndef ZZ_DQ_WAVES
-#define ZZ_DQ_WAVES 2
-#endif
-
 namespace zz {
 namespace {
 
@@ -31,7 +26,7 @@ constexpr int kDqThreads = 512;    // eight waves own 32 query rows each
 // global -> LDS by the memory unit into double buffers (K^T is read from the
 // K tile by LDS transpose reads).
 template <typename T, int D>
-__global__ void __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(ZZ_DQ_WAVES)))
+__global__ void __launch_bounds__(kDqThreads) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(BwdArgs a) {
     using M = Mfma<T, D>;
     constexpr int kKT = k_tile<T, D>();

@@ -237,6 +237,18 @@ zz_status zz_plan_pair_counts(const zz_plan *p, zz_pass pass, int32_t rank, int3
     return ZZ_OK;
 }
 
+zz_status zz_plan_rank_useful_pairs(const zz_plan *p, int64_t *out) {
+    ZZ_TRY(check_plan(p, false));
+    if (!out) return fail(ZZ_ERR_ARG, "null output");
+    const zz::PassTables &t = p->pass[ZZ_PASS_FWD];
+    for (int32_t r = 0; r < p->cp; ++r) {
+        int64_t u = 0;
+        for (int32_t s = 0; s < p->cp; ++s) u += t.useful[(size_t)s * p->cp + r];
+        out[r] = u;
+    }
+    return ZZ_OK;
+}
+
 zz_status zz_zigzag_permute(const zz_plan *p, const void *x_packed, void *x_zz, int64_t row_bytes,
                             void *stream) {
     ZZ_TRY(check_plan(p));

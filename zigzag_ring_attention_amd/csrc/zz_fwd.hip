@@ -22,10 +22,6 @@
 
 #include "zz_mfma.h"
 
-#ifndef ZZ_FWD_WAVES
-#define ZZ_FWD_WAVES 2
-#endif
-
 namespace zz {
 namespace {
 
@@ -52,7 +48,7 @@ struct FwdArgs {
 };
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ZZ_FWD_WAVES)))
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 fwd_step_kernel(FwdArgs a) {
     using M = Mfma<T, D>;
     using DmaKV = Dma<kBN, M::W, kWaves>;
