@@ -120,6 +120,29 @@ size_t zz_plan_workspace_bytes(const zz_plan *plan);
  */
 zz_status zz_plan_upload(zz_plan *plan, void *d_ws, size_t ws_bytes, void *stream);
 
+/* Size of the library's own per-GPU plan workspace (96 MiB). */
+#define ZZ_STATIC_WORKSPACE_BYTES (96u << 20)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture set up ahead, tight serving loops, harnesses that forbid
+ * hipMalloc): zz_plan_upload into the library's own workspace on the current
+ * device instead of a caller buffer.  It allocates nothing: the workspace is
+ * a static device array of ZZ_STATIC_WORKSPACE_BYTES that every GPU the
+ * library runs on holds until the process ends.  The caller still passes
+ * every input and output buffer of the later calls.
+ *  - One workspace per GPU, shared by every plan uploaded this way on it: the
+ *    upload overwrites the tables of the plan bound there before, which from
+ *    then on is refused (ZZ_ERR_STATE) until it is uploaded again.  An upload
+ *    while kernels of the previously bound plan are still running on that
+ *    GPU (another stream) races with them; so do two uploads at once.
+ *  - The plan must then be used with the same device current (ZZ_ERR_STATE
+ *    otherwise); a later zz_plan_upload rebinds it to a caller buffer.
+ * Errors: ZZ_ERR_ARG (null plan), ZZ_ERR_WORKSPACE (zz_plan_workspace_bytes
+ * above ZZ_STATIC_WORKSPACE_BYTES: use zz_plan_upload), ZZ_ERR_HIP.
+ */
+zz_status zz_plan_upload_static(zz_plan *plan, void *stream);
+
 /* Shape queries.  Any output pointer may be NULL. */
 zz_status zz_plan_shape(const zz_plan *plan, int64_t *total_tokens, int32_t *nseq, int32_t *cp,
                         int32_t *hq, int32_t *hkv, int32_t *head_dim, int32_t *dtype);

@@ -61,6 +61,7 @@ def lib():
         "zz_plan_destroy": ([P], None),
         "zz_plan_workspace_bytes": ([P], sz),
         "zz_plan_upload": ([P, P, sz, P], i32),
+        "zz_plan_upload_static": ([P, P], i32),
         "zz_plan_shape": ([P, P, P, P, P, P, P, P], i32),
         "zz_plan_local_cu_seqlens": ([P, P], i32),
         "zz_plan_zigzag_dst": ([P, P], i32),
@@ -166,6 +167,14 @@ class Plan:
         n = self.workspace_bytes()
         self.workspace = torch.empty(n, dtype=torch.uint8, device=device)
         _check(lib().zz_plan_upload(self._h, _ptr(self.workspace), n, _stream()), "zz_plan_upload")
+        return self
+
+    def upload_static(self):
+        """Bind the plan to the library's own per-GPU workspace (no device
+        allocation); another plan uploaded this way on the GPU makes this one
+        stale until it is uploaded again."""
+        _check(lib().zz_plan_upload_static(self._h, _stream()), "zz_plan_upload_static")
+        self.workspace = None
         return self
 
     def local_cu_seqlens(self) -> np.ndarray:

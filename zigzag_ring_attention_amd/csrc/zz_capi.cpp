@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "zz_internal.h"
@@ -19,9 +20,34 @@ zz_status fail(zz_status s, const std::string &msg) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// ------------------------------------------------- static plan workspace
+// The workspace of zz_plan_upload_static, for callers that cannot allocate
+// device memory.  Every GPU the library runs on holds its own copy of this
+// array until the process ends.  In host code the array's name is not a
+// device address: each device's address is looked up once, with that device
+// current, by hipGetSymbolAddress, kept in g_static, and used everywhere
+// host code needs the array (the upload copy, the kernels' table pointers).
+static __device__ __align__(256) uint8_t scratch[ZZ_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct StaticSlot {
+    uint8_t *ptr = nullptr;    // device address of `scratch` on this device
+    uint64_t generation = 0;   // uploads into it so far
+};
+std::mutex g_static_mu;
+StaticSlot g_static[kMaxDevices];
+
 zz_status check_plan(const zz_plan *p, bool need_upload = true) {
     if (!p) return fail(ZZ_ERR_ARG, "null plan");
     if (need_upload && !p->d_ws) return fail(ZZ_ERR_STATE, "plan not uploaded (call zz_plan_upload)");
+    if (need_upload && p->static_dev >= 0) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess || cur != p->static_dev)
+            return fail(ZZ_ERR_STATE, "plan is bound to the static workspace of another device");
+        std::lock_guard<std::mutex> lk(g_static_mu);
+        if (g_static[p->static_dev].generation != p->static_gen)
+            return fail(ZZ_ERR_STATE, "the static workspace now holds another plan's tables; upload this plan again");
+    }
     return ZZ_OK;
 }
 
@@ -127,6 +153,37 @@ zz_status zz_plan_upload(zz_plan *plan, void *d_ws, size_t ws_bytes, void *strea
     // The host image must outlive the copy: wait for it here, once per plan.
     ZZ_TRY(hip_status(hipStreamSynchronize(st), "plan upload sync"));
     plan->d_ws = (const uint8_t *)d_ws;
+    plan->static_dev = -1;
+    return ZZ_OK;
+}
+
+zz_status zz_plan_upload_static(zz_plan *plan, void *stream) {
+    ZZ_TRY(check_plan(plan, false));
+    if (plan->ws_bytes > (size_t)ZZ_STATIC_WORKSPACE_BYTES)
+        return fail(ZZ_ERR_WORKSPACE, "plan workspace of " + std::to_string(plan->ws_bytes) +
+                                          " bytes exceeds the static workspace (" +
+                                          std::to_string((size_t)ZZ_STATIC_WORKSPACE_BYTES) +
+                                          " bytes); use zz_plan_upload");
+    int dev = -1;
+    ZZ_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+    if (dev < 0 || dev >= kMaxDevices) return fail(ZZ_ERR_ARG, "device index beyond the static workspace table");
+    std::lock_guard<std::mutex> lk(g_static_mu);
+    StaticSlot &slot = g_static[dev];
+    if (!slot.ptr) {
+        void *addr = nullptr;
+        ZZ_TRY(hip_status(hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)), "static workspace address"));
+        slot.ptr = static_cast<uint8_t *>(addr);
+    }
+    // Any plan bound here before is stale from now on, even if the copy fails.
+    ++slot.generation;
+    plan->d_ws = nullptr;
+    hipStream_t st = (hipStream_t)stream;
+    ZZ_TRY(hip_status(hipMemcpyAsync(slot.ptr, plan->image.data(), plan->ws_bytes, hipMemcpyHostToDevice, st),
+                      "static plan upload"));
+    ZZ_TRY(hip_status(hipStreamSynchronize(st), "static plan upload sync"));
+    plan->d_ws = slot.ptr;
+    plan->static_dev = dev;
+    plan->static_gen = slot.generation;
     return ZZ_OK;
 }
 

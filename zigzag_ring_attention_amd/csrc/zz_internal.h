@@ -63,6 +63,11 @@ struct zz_plan {
     size_t ws_bytes = 0;
     std::vector<uint8_t> image;  // host image of the device workspace
     const uint8_t *d_ws = nullptr;  // bound device workspace (after upload)
+    // Set by zz_plan_upload_static: the device whose static workspace holds
+    // this plan's tables, and that workspace's upload count at the time (a
+    // later upload into it makes the plan stale).  -1: a caller's workspace.
+    int32_t static_dev = -1;
+    uint64_t static_gen = 0;
 };
 
 namespace zz {
