@@ -19,7 +19,8 @@ Also printed, on the same JSON line:
    mean duration (HIP events around every launch in the timed steps), against
    the bf16 dense MFMA peak of MI355X (2.5 PFLOP/s);
  * per-rank balance: useful pairs per simulated rank from the plan, and the
-   measured time of each rank's forward run in isolation (max/mean);
+   measured time of each rank's forward (and backward) run in isolation,
+   median of four passes (max/mean);
  * cpu_baseline: the CPU oracle (fp64, OpenMP) timed on a bounded sample of
    the same workload's rows, in useful TFLOP/s.
 """
@@ -314,26 +315,53 @@ def main():
 
     balance = None
     if not args.no_balance and not args.gathered:
-        # Each rank's forward steps run alone; ranks are timed in ascending and
-        # then descending order and averaged, so clock or cache drift over the
-        # measurement does not masquerade as imbalance.
-        per_rank_ms = [0.0] * cp
-        for order in (list(range(cp)), list(reversed(range(cp)))):
-            for r in order:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
-                for s in range(cp):
-                    zz.varlen_ring_step_fwd(plan, r, s, q_zz, k_zz, v_zz, o_acc, lse, merge=s > 0)
-                b.record()
-                b.synchronize()
-                per_rank_ms[r] += 0.5 * a.elapsed_time(b)
-        pairs = [plan.pair_counts(r)[0] for r in range(cp)]
+        # Each rank's work runs alone, as it would on a GPU of its own: its
+        # forward steps, and (with the backward) its dK/dV and dQ launches of
+        # every step.  One untimed pass over all ranks first; then four timed
+        # passes in ascending, descending, ascending, descending rank order,
+        # and each rank's median, so clock or cache drift over the measurement
+        # does not masquerade as imbalance.
+        def rank_fwd(r):
+            for s in range(cp):
+                zz.varlen_ring_step_fwd(plan, r, s, q_zz, k_zz, v_zz, o_acc, lse, merge=s > 0)
+
+        def rank_bwd(r):
+            for s in range(cp):
+                zz.varlen_ring_step_bwd_dkv(plan, r, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dk_acc, dv_acc,
+                                            accumulate=s > 0)
+                zz.varlen_ring_step_bwd_dq(plan, r, s, q_zz, k_zz, v_zz, do_zz, lse, delta, dq_acc,
+                                           accumulate=s > 0)
+
+        def per_rank(fn):
+            for r in range(cp):
+                fn(r)
+            torch.cuda.synchronize()
+            times = [[] for _ in range(cp)]
+            for order in (list(range(cp)), list(reversed(range(cp)))) * 2:
+                for r in order:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    fn(r)
+                    b.record()
+                    b.synchronize()
+                    times[r].append(a.elapsed_time(b))
+            return [sorted(t)[len(t) // 2 - 1: len(t) // 2 + 1] for t in times]
+
+        def med(pair):
+            return 0.5 * (pair[0] + pair[1])
+
+        pairs = [int(x) for x in plan.rank_useful_pairs()]
+        fwd_rank = [med(t) for t in per_rank(rank_fwd)]
         balance = {
             "useful_pairs_max_over_mean": max(pairs) / (sum(pairs) / cp),
-            "fwd_ms_per_rank_isolated": [round(x, 3) for x in per_rank_ms],
-            "measured_max_over_mean": max(per_rank_ms) / (sum(per_rank_ms) / cp),
+            "fwd_ms_per_rank_isolated": [round(x, 3) for x in fwd_rank],
+            "measured_max_over_mean": max(fwd_rank) / (sum(fwd_rank) / cp),
         }
+        if backward:
+            bwd_rank = [med(t) for t in per_rank(rank_bwd)]
+            balance["bwd_ms_per_rank_isolated"] = [round(x, 3) for x in bwd_rank]
+            balance["bwd_measured_max_over_mean"] = max(bwd_rank) / (sum(bwd_rank) / cp)
         log("bench: balance %s" % json.dumps(balance))
 
     cpu = None
