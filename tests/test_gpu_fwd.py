@@ -23,6 +23,11 @@ def oracle_packed_fwd(case):
     ((8, 24, 16), 4, 3, 64, "bf16"),
     (tuple(synthetic.lengths_for(synthetic.WORKLOADS["c2"])), 4, 16, 128, "bf16"),
     ((2, 2, 4), 1, 1, 32, "f32"),
+    # wide rows (16-byte vectors per row 640, 1024, 768): the permute's
+    # eight-deep loop with and without a tail
+    ((64, 192, 128), 4, 40, 128, "bf16"),
+    ((96, 32), 2, 64, 128, "bf16"),
+    ((48, 16), 2, 24, 128, "f32"),
 ])
 def test_permute_unpermute_bit_exact(lengths, cp, h, d, dtype):
     import torch
@@ -36,6 +41,20 @@ def test_permute_unpermute_bit_exact(lengths, cp, h, d, dtype):
     assert np.array_equal(got, want)
     back = zz.zigzag_unpermute(plan, xz)
     assert torch.equal(back.cpu(), x)
+
+
+@pytest.mark.parametrize("hq,dtype", [(4, "bf16"), (40, "bf16"), (64, "bf16"), (24, "f32")])
+def test_finalize_fwd_casts_and_unpermutes_bit_exact(hq, dtype):
+    """fp32 rows -> plan dtype by round-to-nearest-even (torch's cast), in
+    zigzag or packed order; hq 40/64 at head_dim 128 make rows of 1280/2048
+    four-float vectors (the cast kernel's unrolled loop and its tail)."""
+    import torch
+    cu = synthetic.make_cu_seqlens((64, 192, 128))
+    plan = zz.Plan(cu, 4, hq, 1, 128, dtype, device="cuda")
+    o = torch.randn((plan.total, hq, 128), generator=torch.Generator().manual_seed(6)).cuda()
+    want = o.to(plan.torch_dtype)
+    assert torch.equal(zz.finalize_fwd(plan, o, unpermute=False), want)
+    assert torch.equal(zz.finalize_fwd(plan, o, unpermute=True), zz.zigzag_unpermute(plan, want))
 
 
 # ------------------------------------------------------------------ masks
