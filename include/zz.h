@@ -30,8 +30,9 @@
  *    LSE and delta are fp32 [Hq, T] (natural log), indexed by zigzag row.
  *    Query head h uses key/value head h / (Hq/Hkv).
  *  - Ownership.  The caller owns every device buffer, including the plan
- *    workspace.  libzz allocates no device memory.  libzz owns the plan's host
- *    memory; zz_plan_destroy frees it.
+ *    workspace (except with zz_plan_upload_static, whose workspace is a
+ *    static array of the library).  libzz allocates no device memory.  libzz
+ *    owns the plan's host memory; zz_plan_destroy frees it.
  *  - Errors.  Every call returns zz_status; nothing throws across the ABI.
  *    Arguments are checked on the host before any launch; device pointers
  *    must be 16-byte aligned (ZZ_ERR_ALIGN).  A buffer a call writes must
