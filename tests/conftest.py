@@ -11,6 +11,8 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long CPU oracle work")
+    import zz_testlib
+    zz_testlib.set_capture_manager(config.pluginmanager.getplugin("capturemanager"))
 
 
 def pytest_collection_modifyitems(config, items):

@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import synthetic
-from zz_testlib import TOL, check_grad, max_abs, rel_l2, to_np
+from zz_testlib import TOL, check_grad, max_abs, progress, rel_l2, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -94,7 +94,7 @@ def head_reference(name, head):
         rows = np.arange(a, b, dtype=np.int64)
         o[a:b], lse[a:b] = oracle.attn_fwd_rows(s.q, s.k, s.v, s.cu, s.w.scale, rows,
                                                 np.full(b - a, head, dtype=np.int32))
-        print("oracle %s head %d: rows %d..%d done (%d/%d)" % (name, head, a, b, c + 1, nchunk), flush=True)
+        progress("oracle %s head %d: rows %d..%d done (%d/%d)" % (name, head, a, b, c + 1, nchunk))
     return o, lse
 
 

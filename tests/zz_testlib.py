@@ -6,6 +6,23 @@ import numpy as np
 
 import synthetic
 
+_capture = None   # pytest's capture manager (set by conftest.py)
+
+
+def set_capture_manager(capman) -> None:
+    global _capture
+    _capture = capman
+
+
+def progress(msg: str) -> None:
+    """Print a progress line past pytest's output capture, so a test that
+    runs the oracle for minutes keeps writing to the terminal (or log)."""
+    if _capture is None:
+        print(msg, flush=True)
+        return
+    with _capture.global_and_fixture_disabled():
+        print(msg, flush=True)
+
 
 class Case:
     """One seeded workload: CPU inputs (the oracle's copy) and device tensors."""
