@@ -17,7 +17,6 @@ struct BwdArgs {
     const float *lse, *delta;
     float *dq, *dk, *dv;
     const WorkItem *items;
-    const int32_t *order;
     const TileRec *tiles;
     int64_t T;
     int32_t n, hq, hkv;

@@ -68,7 +68,7 @@ bwd_dkv_kernel(BwdArgs a) {
     int item_ix, kvh;
     block_to_work(blockIdx.x, a.nitems, a.hkv, 1, item_ix, kvh);
     const int G = a.hq / a.hkv;
-    const WorkItem it = load_const(a.items, a.order ? load_const(a.order, item_ix) : item_ix);
+    const WorkItem it = load_const(a.items, item_ix);
     const int nkey = it.a1 - it.a0;
     const int kk = pair * 32 + (lane & 31);          // key offset in the item
     const bool key_ok = kk < nkey;
@@ -260,7 +260,7 @@ hipError_t launch_t(const zz_plan *p, int base, int rank, int step, BwdArgs a, i
     const int pkv = base + ZZ_PASS_BWD_DKV, pq = base + ZZ_PASS_BWD_DQ;
     const Launch Lkv = launch_items(p, pkv, rank, step);
     if ((which & 1) && Lkv.n > 0) {
-        a.items = Lkv.items; a.order = Lkv.order; a.tiles = dev_tiles(p, pkv); a.nitems = Lkv.n;
+        a.items = Lkv.items; a.tiles = dev_tiles(p, pkv); a.nitems = Lkv.n;
         hipLaunchKernelGGL((bwd_dkv_kernel<T, D>), dim3(Lkv.n * p->hkv), dim3(kDkvThreads), 0, st, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -275,7 +275,7 @@ hipError_t launch_bwd_pass(const zz_plan *p, int base, int rank, int step, const
     BwdArgs a;
     a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse; a.delta = delta;
     a.dq = dq; a.dk = dk; a.dv = dv;
-    a.items = nullptr; a.order = nullptr; a.tiles = nullptr;
+    a.items = nullptr; a.tiles = nullptr;
     a.T = p->T; a.n = (int32_t)(p->T / p->cp); a.hq = p->hq; a.hkv = p->hkv;
     a.scale = (float)(1.0 / std::sqrt((double)p->d));
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));

@@ -43,7 +43,7 @@ bwd_dq_kernel(BwdArgs a) {
     int item_ix, head;
     block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
     const int kvh = head / (a.hq / a.hkv);
-    const WorkItem it = load_const(a.items, a.order ? load_const(a.order, item_ix) : item_ix);
+    const WorkItem it = load_const(a.items, item_ix);
     const int nq = it.a1 - it.a0;
     const int qq = wave * 32 + (lane & 31);
     const bool row_ok = qq < nq;
@@ -88,9 +88,14 @@ bwd_dq_kernel(BwdArgs a) {
         if (wave_on) {
 #pragma unroll
             for (int kb = 0; kb < kKT / 32; ++kb) {
+                // dP^T accumulates onto -delta (one value per lane: the lane's
+                // query), so the chain yields dP - delta directly
                 f32x16 s, dp;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.0f;
+                for (int i = 0; i < 16; ++i) {
+                    s[i] = 0.0f;
+                    dp[i] = -dlt;
+                }
                 M::gemm_rows_lds_pair(s, ks, qop, dp, vs, dop, kb * 32 + (lane & 31), hh);
                 // mask (partial and ragged tiles only): key kk is kept iff kk < nk
                 // and, in a partial tile, kk <= qq + delta; rows of queries past
@@ -101,7 +106,7 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const float p = __builtin_amdgcn_exp2f(fmaf(s[i], a.scale_log2, -lse2));
-                    dp[i] = p * (dp[i] - dlt);
+                    dp[i] = p * dp[i];
                 }
                 M::gemm_t_c(acc, ks, kb * 32, dp, lane);
             }
@@ -124,7 +129,7 @@ template <typename T, int D>
 hipError_t launch_t(const zz_plan *p, int pass, int rank, int step, BwdArgs a, hipStream_t st) {
     const Launch L = launch_items(p, pass, rank, step);
     if (L.n == 0) return hipSuccess;
-    a.items = L.items; a.order = L.order; a.tiles = dev_tiles(p, pass); a.nitems = L.n;
+    a.items = L.items; a.tiles = dev_tiles(p, pass); a.nitems = L.n;
     hipLaunchKernelGGL((bwd_dq_kernel<T, D>), dim3(L.n * p->hq), dim3(kDqThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -37,7 +37,6 @@ struct FwdArgs {
     const void *q, *k, *v;
     float *o, *lse;
     const WorkItem *items;
-    const int32_t *order;
     const TileRec *tiles;
     int64_t T;          // total tokens
     int32_t n;          // rows per rank = T / cp
@@ -63,7 +62,7 @@ fwd_step_kernel(FwdArgs a) {
     int item_ix, head;
     block_to_work(blockIdx.x, a.nitems, a.hq, a.hq / a.hkv, item_ix, head);
     const int kvh = head / (a.hq / a.hkv);
-    const WorkItem it = load_const(a.items, a.order ? load_const(a.order, item_ix) : item_ix);
+    const WorkItem it = load_const(a.items, item_ix);
     const int nq = it.a1 - it.a0;
     const int qq = wave * 32 + (lane & 31);          // query offset in the item
     const bool row_ok = qq < nq;
@@ -219,7 +218,7 @@ hipError_t launch_t(const zz_plan *p, const Launch &L, const TileRec *tiles, con
                     const void *v, float *o, float *lse, int merge, hipStream_t st) {
     FwdArgs a;
     a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-    a.items = L.items; a.order = L.order; a.tiles = tiles;
+    a.items = L.items; a.tiles = tiles;
     a.T = p->T; a.n = (int32_t)(p->T / p->cp); a.hq = p->hq; a.hkv = p->hkv;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
     a.merge = merge;

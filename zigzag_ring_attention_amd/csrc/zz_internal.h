@@ -39,12 +39,12 @@ struct PassTables {
     bool keep_empty = false;     // list stationary tiles with no visible tile (FWD)
     std::vector<WorkItem> items; // grouped by (step, rank); LPT order inside a rank
     std::vector<TileRec> tiles;
-    std::vector<int32_t> order;  // per step: item ids, LPT over all ranks
+    std::vector<WorkItem> ordered;   // per step: every rank's items in launch order
     std::vector<int64_t> rank_off;   // [(step*cp + rank)] -> first item; size cp*cp+1
-    std::vector<int64_t> order_off;  // [step] -> first entry of order; size cp+1
+    std::vector<int64_t> order_off;  // [step] -> first entry of `ordered`; size cp+1
     std::vector<int64_t> useful;     // [(step*cp + rank)] visible pairs (per head)
     std::vector<int64_t> issued;     // [(step*cp + rank)] pairs covered by visited tiles
-    size_t off_items = 0, off_tiles = 0, off_order = 0;  // byte offsets in the workspace
+    size_t off_items = 0, off_tiles = 0, off_ordered = 0;  // byte offsets in the workspace
 };
 
 }  // namespace zz
@@ -91,15 +91,15 @@ inline const WorkItem *dev_items(const zz_plan *p, int pass) {
 inline const TileRec *dev_tiles(const zz_plan *p, int pass) {
     return reinterpret_cast<const TileRec *>(p->d_ws + p->pass[pass].off_tiles);
 }
-inline const int32_t *dev_order(const zz_plan *p, int pass) {
-    return reinterpret_cast<const int32_t *>(p->d_ws + p->pass[pass].off_order);
+inline const WorkItem *dev_ordered(const zz_plan *p, int pass) {
+    return reinterpret_cast<const WorkItem *>(p->d_ws + p->pass[pass].off_ordered);
 }
 
-// Item selection of one launch: either a contiguous range of items (one rank)
-// or, for all ranks, the step's LPT order list.
+// Item selection of one launch: a contiguous range of work items, one
+// rank's (in its longest-first order) or, for all ranks, the step's items in
+// launch order.
 struct Launch {
     const WorkItem *items;
-    const int32_t *order;  // null: items[blockIdx] directly
     int32_t n;
 };
 Launch launch_items(const zz_plan *p, int pass, int rank, int step);

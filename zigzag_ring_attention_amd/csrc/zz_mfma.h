@@ -90,9 +90,12 @@ typedef __attribute__((address_space(3))) char lds_char;
 // use of it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// The LDS destination is lds + IMM: the per-instruction part is an immediate,
+// so the kernels keep one scalar register per tile buffer, not one per block.
+template <uint32_t IMM>
 __device__ __forceinline__ void dma_block(const char *base, uint32_t off, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(off), "s"(base), "s"(lds) : "memory", "m0");
+    asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(base), "s"(lds), "i"(IMM) : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
 
@@ -124,17 +127,18 @@ template <int ROWS, int W, int NW> struct Dma {
         const int sl = (pu % W) ^ Swz<W>::key(r);
         return (uint32_t)min(r, nrows - 1) * gstride + (uint32_t)(sl * 16);
     }
+    template <int J, bool FULL>
+    __device__ __forceinline__ void issue_from(const char *base, int nrows, uint32_t l0) const {
+        if constexpr (J < PER) {
+            if (INSTR % NW == 0 || J * NW + w < INSTR)
+                dma_block<(uint32_t)(J * NW * 1024)>(base, FULL ? off[J] : offset(J, nrows), l0);
+            issue_from<J + 1, FULL>(base, nrows, l0);
+        }
+    }
     __device__ __forceinline__ void issue(const char *base, int nrows, const void *lds) const {
         const uint32_t l0 = lds_addr(lds) + (uint32_t)w * 1024u;
-        if (nrows >= ROWS) {
-#pragma unroll
-            for (int j = 0; j < PER; ++j)
-                if (INSTR % NW == 0 || j * NW + w < INSTR) dma_block(base, off[j], l0 + j * NW * 1024);
-        } else {
-#pragma unroll
-            for (int j = 0; j < PER; ++j)
-                if (INSTR % NW == 0 || j * NW + w < INSTR) dma_block(base, offset(j, nrows), l0 + j * NW * 1024);
-        }
+        if (nrows >= ROWS) issue_from<0, true>(base, nrows, l0);
+        else issue_from<0, false>(base, nrows, l0);
     }
 };
 

@@ -106,7 +106,7 @@ void build_pass(zz_plan *p, PassTables &t) {
     const int32_t cp = p->cp;
     t.items.clear();
     t.tiles.clear();
-    t.order.clear();
+    t.ordered.clear();
     t.rank_off.assign((size_t)cp * cp + 1, 0);
     t.order_off.assign((size_t)cp + 1, 0);
     t.useful.assign((size_t)cp * cp, 0);
@@ -171,15 +171,15 @@ void build_pass(zz_plan *p, PassTables &t) {
             std::copy(tw.begin(), tw.end(), item_work.begin() + first_item);
         }
         // Whole-step launch order over every rank.
-        t.order_off[s] = (int64_t)t.order.size();
+        t.order_off[s] = (int64_t)t.ordered.size();
         const int64_t b = t.rank_off[(size_t)s * cp], e = (int64_t)t.items.size();
         std::vector<int32_t> ord;
         for (int64_t u = b; u < e; ++u) ord.push_back((int32_t)u);
         launch_order(p, t, item_work, ord);
-        t.order.insert(t.order.end(), ord.begin(), ord.end());
+        for (int32_t u : ord) t.ordered.push_back(t.items[(size_t)u]);
     }
     t.rank_off[(size_t)cp * cp] = (int64_t)t.items.size();
-    t.order_off[cp] = (int64_t)t.order.size();
+    t.order_off[cp] = (int64_t)t.ordered.size();
 }
 
 // Gathered walks: every stationary item of rank r (its query rows for the
@@ -196,7 +196,7 @@ void build_gathered_pass(zz_plan *p, PassTables &t) {
     const int64_t n = p->T / cp;
     t.items.clear();
     t.tiles.clear();
-    t.order.clear();
+    t.ordered.clear();
     t.rank_off.assign((size_t)cp + 1, 0);
     t.order_off.assign(2, 0);
     t.useful.assign((size_t)cp, 0);
@@ -261,8 +261,8 @@ void build_gathered_pass(zz_plan *p, PassTables &t) {
     std::vector<int32_t> ord;
     for (size_t u = 0; u < t.items.size(); ++u) ord.push_back((int32_t)u);
     launch_order(p, t, item_work, ord);
-    t.order = ord;
-    t.order_off[1] = (int64_t)t.order.size();
+    for (int32_t u : ord) t.ordered.push_back(t.items[(size_t)u]);
+    t.order_off[1] = (int64_t)t.ordered.size();
 }
 
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -335,7 +335,7 @@ zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, in
     for (auto &t : p->pass) {
         t.off_items = off; off = align_up(off + sizeof(WorkItem) * t.items.size());
         t.off_tiles = off; off = align_up(off + sizeof(TileRec) * t.tiles.size());
-        t.off_order = off; off = align_up(off + sizeof(int32_t) * t.order.size());
+        t.off_ordered = off; off = align_up(off + sizeof(WorkItem) * t.ordered.size());
     }
     p->ws_bytes = std::max<size_t>(off, 256);
     p->image.assign(p->ws_bytes, 0);
@@ -343,7 +343,8 @@ zz_status build_plan(const int32_t *cu, int32_t nseq, int32_t cp, int32_t hq, in
     for (auto &t : p->pass) {
         if (!t.items.empty()) std::memcpy(p->image.data() + t.off_items, t.items.data(), sizeof(WorkItem) * t.items.size());
         if (!t.tiles.empty()) std::memcpy(p->image.data() + t.off_tiles, t.tiles.data(), sizeof(TileRec) * t.tiles.size());
-        if (!t.order.empty()) std::memcpy(p->image.data() + t.off_order, t.order.data(), sizeof(int32_t) * t.order.size());
+        if (!t.ordered.empty())
+            std::memcpy(p->image.data() + t.off_ordered, t.ordered.data(), sizeof(WorkItem) * t.ordered.size());
     }
     *out = p;
     return ZZ_OK;
@@ -354,10 +355,10 @@ Launch launch_items(const zz_plan *p, int pass, int rank, int step) {
     const int cp = p->cp;
     if (rank < 0) {
         const int64_t b = t.order_off[step], e = t.order_off[step + 1];
-        return Launch{dev_items(p, pass), dev_order(p, pass) + b, (int32_t)(e - b)};
+        return Launch{dev_ordered(p, pass) + b, (int32_t)(e - b)};
     }
     const int64_t b = t.rank_off[(size_t)step * cp + rank], e = t.rank_off[(size_t)step * cp + rank + 1];
-    return Launch{dev_items(p, pass) + b, nullptr, (int32_t)(e - b)};
+    return Launch{dev_items(p, pass) + b, (int32_t)(e - b)};
 }
 
 }  // namespace zz
