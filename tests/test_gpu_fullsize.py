@@ -205,10 +205,12 @@ def test_forward_zero_query_closed_form_full_size(name):
 
 # ----------------------------------------------------------------- backward
 
-@pytest.mark.parametrize("name", ["c4", "c5"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
 def test_backward_sampled_dq_rows(name):
-    """c4: 65536 tokens packed from 15 documents (document mask), GQA 64/8;
-    c5: one 131072-token sequence, GQA 64/8.  512 (row, head) pairs."""
+    """c3: one 32768-token sequence, GQA 32/8 (its own configuration is
+    forward-only; dO drawn after Q, K, V as for c5); c4: 65536 tokens packed
+    from 15 documents (document mask), GQA 64/8; c5: one 131072-token
+    sequence, GQA 64/8.  512 (row, head) pairs."""
     s = setup(name, with_do=True)
     w = s.w
     dq, dk, dv = s.backward()
@@ -239,17 +241,17 @@ def test_backward_c4_sampled_dkv_rows():
 
 
 @pytest.mark.timeout(900)
-def test_backward_c5_one_head_sampled_rows():
-    """c5 (the benchmarked configuration) with dO zero on every query head
-    but one: that head's group gets its dK, dV from that head alone.  Compared:
-    512 key rows of dK and dV (every chunk's first and last row included) and
-    512 dQ rows of the head; every other head's dQ and every other group's dK,
-    dV must be exactly zero."""
+@pytest.mark.parametrize("name,h", [("c3", 29), ("c5", 61)])
+def test_backward_one_head_sampled_rows(name, h):
+    """c5 (the benchmarked configuration) and c3 with dO zero on every query
+    head but one: that head's group gets its dK, dV from that head alone.
+    Compared: 512 key rows of dK and dV (every chunk's first and last row
+    included) and 512 dQ rows of the head; every other head's dQ and every
+    other group's dK, dV must be exactly zero."""
     import torch
-    s = setup("c5", with_do=True)
+    s = setup(name, with_do=True)
     w = s.w
     G = w.hq // w.hkv
-    h = 61
     g = h // G
     keep = torch.zeros((1, w.hq, 1), dtype=s.doz.dtype, device=s.doz.device)
     keep[0, h, 0] = 1
@@ -260,23 +262,23 @@ def test_backward_c5_one_head_sampled_rows():
     rows, _ = sample_rows(s.cu, w.cp, 512, [0], 59)
     kvh = np.full(len(rows), g, dtype=np.int32)
     wk, wv = oracle.attn_bwd_dkv_rows(s.q, s.k, s.v, do, s.cu, w.scale, rows, kvh, heads_on=[h],
-                                      row_stats=row_stats("c5", [h], do))
+                                      row_stats=row_stats(name, [h], do))
     zr = s.dst[rows]
-    tag = "c5 head %d key rows=%d" % (h, len(rows))
+    tag = "%s head %d key rows=%d" % (name, h, len(rows))
     check_grad("dk", dk[zr, g].float().cpu().numpy(), wk, TOL_BF16, 1.0, tag)
     check_grad("dv", dv[zr, g].float().cpu().numpy(), wv, TOL_BF16, 1.0, tag)
     qrows, _ = sample_rows(s.cu, w.cp, 512, [0], 61)
     wq = oracle.attn_bwd_dq_rows(s.q, s.k, s.v, do, s.cu, w.scale, qrows,
                                  np.full(len(qrows), h, dtype=np.int32))
     check_grad("dq", dq[s.dst[qrows], h].float().cpu().numpy(), wq, TOL_BF16, 1.0,
-               "c5 head %d rows=%d" % (h, len(qrows)))
+               "%s head %d rows=%d" % (name, h, len(qrows)))
     others_q = [x for x in range(w.hq) if x != h]
     others_kv = [x for x in range(w.hkv) if x != g]
     assert float(dq[:, others_q].abs().max()) == 0.0
     assert float(dk[:, others_kv].abs().max()) == 0.0 and float(dv[:, others_kv].abs().max()) == 0.0
 
 
-@pytest.mark.parametrize("name", ["c4", "c5"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
 def test_backward_gradient_identities(name):
     """Exact identities of the attention gradient, per key/value group (they
     hold per document, hence also summed over a packed batch):
