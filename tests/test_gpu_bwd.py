@@ -55,6 +55,15 @@ def test_backward_bf16(lengths, cp, hq, hkv, d, q_scale):
     check_grads(case, TOL["bf16"], q_scale)
 
 
+def test_backward_c2_full():
+    """The c2 packing (8192 tokens in 5 documents, 16/16 heads, head_dim 128,
+    CP 4; dO drawn after Q, K, V): every element of dQ, dK and dV against
+    the oracle's backward, at the flat gate."""
+    w = synthetic.WORKLOADS["c2"]
+    case = Case(tuple(synthetic.lengths_for(w)), w.cp, w.hq, w.hkv, w.d, w.dtype, w.seed, with_do=True)
+    check_grads(case, TOL["bf16"])
+
+
 def test_backward_with_dq_on_a_second_stream_is_bitwise_equal():
     import torch
     case = Case((64, 320, 128, 96), 4, 4, 2, 128, "bf16", 7, with_do=True)
